@@ -1,0 +1,68 @@
+"""Seeded synthetic inputs for the GEMM workloads.
+
+This module holds no GEMM arithmetic: it only draws matrices from a seeded
+CPU ``torch.Generator`` and casts them (round-to-nearest-even) to the stored
+dtype.  Both the oracle-side tests and the GPU-side tests and benchmark take
+their inputs from here, so the two sides read the same bits.
+
+Distributions (per workload):
+
+* ``"uniform"``  -- i.i.d. U(-1, 1)
+* ``"normal"``   -- i.i.d. N(0, 1)
+* ``"normal_k"`` -- i.i.d. N(0, 1) / sqrt(K)   (``scale_k`` gives K)
+* ``"int2"``     -- i.i.d. integers uniform in {-2, ..., 2}
+
+Seeds follow ``1000 * workload + role`` with role 1 = A, 2 = B, 3 = C_in;
+integer twins add 100.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def seed_for(workload: int, role: str, integer_twin: bool = False) -> int:
+    return 1000 * workload + {"A": 1, "B": 2, "C": 3}[role] + (100 if integer_twin else 0)
+
+
+def draw(rows: int, cols: int, dist: str, seed: int, dtype: str = "f32", *, ld: int | None = None,
+         scale_k: int | None = None) -> torch.Tensor:
+    """A rows x cols CPU tensor of ``dtype``; with ``ld > cols`` it is a view
+    into a rows x ld buffer (the padding holds a recognisable fill value)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    width = cols if ld is None else ld
+    if width < cols:
+        raise ValueError("ld must be >= cols")
+    shape = (rows, width)
+    if dist == "uniform":
+        x = torch.rand(shape, generator=g, dtype=torch.float32) * 2.0 - 1.0
+    elif dist == "normal":
+        x = torch.randn(shape, generator=g, dtype=torch.float32)
+    elif dist == "normal_k":
+        x = torch.randn(shape, generator=g, dtype=torch.float32) / math.sqrt(max(scale_k or 1, 1))
+    elif dist == "int2":
+        x = torch.randint(-2, 3, shape, generator=g, dtype=torch.int32).to(torch.float32)
+    else:
+        raise ValueError(f"unknown distribution {dist!r}")
+    if width > cols:
+        x[:, cols:] = 1.0e30 if dtype == "f32" else 3.0e4  # never read by a correct GEMM
+    x = x.to(DTYPES[dtype])
+    return x[:, :cols] if width > cols else x
+
+
+def as_numpy_bits(t: torch.Tensor):
+    """Stored bits of a CPU tensor as numpy (float32, or uint16 for f16/bf16),
+    keeping the row stride (leading dimension)."""
+    import numpy as np
+    if t.dtype == torch.float32:
+        return t.numpy()
+    if t.dtype in (torch.float16, torch.bfloat16):
+        base = t.view(torch.int16)
+        return base.numpy().view(np.uint16)
+    if t.dtype == torch.float64:
+        return t.numpy()
+    raise TypeError(t.dtype)
