@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Throughput of the dense GEMM hot path on one MI355X.
+
+A step is one pass over the two workloads the headline metric names, each a
+full call of the library (plan, tile schedule, HBM->LDS staging, MFMA inner
+product, alpha/beta epilogue):
+
+  * fp32 SGEMM, row-major NN, M=N=8192, K=4096, alpha=1, beta=0, N(0,1) inputs;
+  * fp16-input HGEMM, TN, M=N=K=4096, fp32 accumulate, fp16 C, N(0,1)/sqrt(K).
+
+Inputs are seeded synthetic matrices, resident in HBM before timing starts.
+``value`` is the whole step's throughput, 2*M*N*K summed over both GEMMs per
+second, in TFLOPS.  The JSON line also carries each part's TFLOPS and its
+fraction of MI355X's dense peak for its dtype, the roofline of the dominant
+kernel (its average launch time from HIP events recorded on the launch
+stream) and the CPU oracle timed on a bounded sample of the same step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+                       [--workload NAME ...]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gemm_inputs as gi  # noqa: E402
+
+METRIC = "GEMM TFLOPS & % of peak: fp32 8192×8192×4096, fp16 4096³ (1 MI355X)"
+STEP = ("fp32_nn_8192x8192x4096", "fp16_tn_4096")
+# MI355X dense peaks (TFLOP/s) per input type, and HBM bandwidth (GB/s).
+PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6}
+HBM_GBPS = 8000.0
+# The pages' own numbers for these workloads (RTX 4090; context only).
+PAGES_CONTEXT = {
+    "fp32_nn_8192x8192x4096": "RTX 4090: 41.9 TFLOPS hand-written (dbuf), 48.7-51.2 cuBLAS",
+    "fp16_tn_4096": "RTX 4090: 148.5 TFLOPS (mma + smem swizzle, fp16 acc), 204 (warp-specialised)",
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def flops(w):
+    return 2.0 * w["M"] * w["N"] * w["K"]
+
+
+def min_bytes(w):
+    """Compulsory HBM traffic: read A, B (and C when beta != 0), write C."""
+    es = 4 if w["in_dtype"] == "f32" else 2
+    ec = 4 if w["c_dtype"] == "f32" else 2
+    M, N, K = w["M"], w["N"], w["K"]
+    return M * K * es + K * N * es + (M * N * ec if w["beta"] != 0 else 0) + M * N * ec
+
+
+def kernel_src_hash():
+    """Hash of the kernel sources and build flags: counter data taken from an
+    older build no longer describes the current kernels."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dense_gemm_12_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    with open(os.path.join(ROOT, "dense_gemm_12_amd", "build.py"), "rb") as fh:
+        h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(config_name, workload):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = data.get(workload)
+    if not rec or rec.get("config") != config_name or rec.get("src_hash") != kernel_src_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(parts, target_s):
+    """The oracle (as it stands) on a row slab of every part of the step."""
+    import oracle
+    threads = oracle.default_threads()
+    total_flops, total_s, desc = 0.0, 0.0, []
+    per_part = target_s / len(parts)
+    for name, (A, B, C) in parts:
+        w = gi.WORKLOADS[name]
+        kw = dict(a_dtype=w["in_dtype"], trans_a=w["ta"], trans_b=w["tb"], alpha=w["alpha"],
+                  beta=w["beta"], c_dtype=w["c_dtype"], M=w["M"], N=w["N"], K=w["K"])
+        bits = lambda t: None if t is None else gi.as_numpy_bits(t)
+        An, Bn, Cn = bits(A), bits(B), bits(C)
+        # size the slab from two trial slabs (fixed cost + cost per row)
+        pts = []
+        rows = max(threads, 8)
+        while True:
+            n = min(rows, w["M"])
+            t0 = time.perf_counter()
+            oracle.gemm(An, Bn, C=Cn, rows=(0, n), threads=threads, **kw)
+            pts.append((n, time.perf_counter() - t0))
+            if (len(pts) >= 2 and pts[-1][1] > per_part / 10) or n >= w["M"]:
+                break
+            rows *= 4
+        (n0, t0_), (n1, t1_) = (pts[-2] if len(pts) > 1 else (0, 0.0)), pts[-1]
+        per_row = (t1_ - t0_) / max(n1 - n0, 1)
+        if per_row <= 0:
+            per_row = t1_ / max(n1, 1)
+        fixed = max(t1_ - n1 * per_row, 0.0)
+        rows = int(min(w["M"], max(1, (per_part - fixed) / per_row)))
+        t0 = time.perf_counter()
+        oracle.gemm(An, Bn, C=Cn, rows=(0, rows), threads=threads, **kw)
+        dt = time.perf_counter() - t0
+        f = 2.0 * rows * w["N"] * w["K"]
+        total_flops += f
+        total_s += dt
+        desc.append(f"{name}: rows 0..{rows} of {w['M']} ({f / 1e9:.1f} GFLOP, {dt:.1f} s)")
+    return {"value": total_flops / total_s / 1e12, "unit": "TFLOPS", "cores": threads,
+            "kind": "oracle", "sample": "; ".join(desc) + "; fp64 triple loop, threads over rows",
+            "seconds": round(total_s, 2), "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--workload", nargs="*", default=None,
+                    help=f"named workloads instead of the metric's step {STEP}")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the GEMM is not sharded "
+              "across GPUs in this library.", file=sys.stderr)
+        sys.exit(2)
+    rank = int(os.environ.get("RANK", "0"))
+
+    import torch
+    import dense_gemm_12_amd as mg
+    mg.load()
+    dev = torch.device("cuda:0")
+    names = tuple(args.workload) if args.workload else STEP
+
+    parts_host, parts_dev, calls = [], [], []
+    for name in names:
+        w = gi.WORKLOADS[name]
+        log(f"inputs {name}")
+        A, B, C = gi.workload_inputs(name)
+        parts_host.append((name, (A, B, C)))
+        Ad, Bd = A.to(dev), B.to(dev)
+        Cd = (C.to(dev) if C is not None else
+              torch.empty((w["M"], w["N"]), dtype=gi.DTYPES[w["c_dtype"]], device=dev))
+        parts_dev.append((Ad, Bd, Cd))
+        calls.append((name, w, Ad, Bd, Cd))
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(evs=None):
+        for i, (name, w, Ad, Bd, Cd) in enumerate(calls):
+            if evs is not None:
+                evs[i][0].record(stream)
+            mg.gemm(Ad, Bd, Cd, alpha=w["alpha"], beta=w["beta"], trans_a=w["ta"],
+                    trans_b=w["tb"], stream=stream)
+            if evs is not None:
+                evs[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in calls]
+              for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    step_flops = sum(flops(w) for _, w, *_ in calls)
+    value = args.steps * step_flops / elapsed / 1e12
+    parts = []
+    for i, (name, w, *_r) in enumerate(calls):
+        ms = sum(events[k][i][0].elapsed_time(events[k][i][1]) for k in range(args.steps)) / args.steps
+        cfg = mg.chosen_config(w["in_dtype"], w["c_dtype"], int(w["ta"]), int(w["tb"]), w["M"],
+                               w["N"], w["K"])
+        tf = flops(w) / (ms * 1e-3) / 1e12
+        parts.append({"workload": name, "kernel": mg.config_name(w["in_dtype"], cfg),
+                      "us_per_launch": round(ms * 1e3, 2), "tflops": round(tf, 2),
+                      "peak_tflops": PEAK_TFLOPS[w["in_dtype"]],
+                      "frac_of_peak": round(tf / PEAK_TFLOPS[w["in_dtype"]], 4),
+                      "min_hbm_bytes": min_bytes(w),
+                      "pages_context": PAGES_CONTEXT.get(name)})
+    dom = max(range(len(parts)), key=lambda i: parts[i]["us_per_launch"])
+    d, dw = parts[dom], calls[dom][1]
+    traffic = load_traffic(d["kernel"], d["workload"])
+    roofline = {"bound": "mfma", "achieved": d["tflops"], "peak": d["peak_tflops"],
+                "unit": "TFLOP/s", "frac": d["frac_of_peak"], "traffic": traffic,
+                "kernel": d["kernel"], "workload": d["workload"],
+                "algorithmic_flops_per_launch": flops(dw)}
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "+".join(sorted({w["in_dtype"] for _, w, *_ in calls})),
+        "data": "synthetic: seeded fp32 N(0,1) and fp16 N(0,1)/sqrt(K) matrices, resident in HBM",
+        "config": {"workload": " + ".join(names), "parts": list(names)},
+        "parts": parts, "roofline": roofline,
+    }
+    if not args.no_cpu and rank == 0:
+        log("CPU oracle baseline")
+        out["cpu_baseline"] = cpu_baseline(parts_host, args.cpu_seconds)
+    if rank == 0:
+        print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,39 @@
+// Launch parameters shared by the host planner and the kernels, and the
+// registry of compiled kernel configurations.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mg {
+
+struct GemmParams {
+  const void *A;
+  const void *B;
+  void *C;
+  int64_t lda, ldb, ldc;  // elements
+  int M, N, K;
+  float alpha, beta;
+  int tiles_m, tiles_n;   // grid = tiles_m * tiles_n workgroups
+  int group_m;            // tile-rows per raster group
+  int c_vec;              // C rows allow 16-byte (fp32) / 8-byte (16-bit) access
+};
+
+typedef hipError_t (*LaunchFn)(const GemmParams &, hipStream_t);
+
+// One compiled tile configuration; fn[c_is_f32][a_kc][b_kc] covers the
+// output type and the four storage layouts.  a_vec / b_vec tell whether the
+// variant needs 16-byte-loadable operands.
+struct KernelEntry {
+  const char *name;
+  int bm, bn, bk;
+  bool a_vec, b_vec;
+  LaunchFn fn[2][2][2];
+};
+
+const KernelEntry *entries_f32(int *n);
+const KernelEntry *entries_f16(int *n);
+const KernelEntry *entries_bf16(int *n);
+
+LaunchFn scale_launcher(int c_dtype);  // 0 = f32, 1 = f16, 2 = bf16
+
+}  // namespace mg

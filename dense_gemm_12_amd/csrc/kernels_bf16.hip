@@ -1,0 +1,22 @@
+// bf16-input GEMM configurations: v_mfma_f32_16x16x32_bf16, fp32 accumulate,
+// BK = 64 (128-byte LDS rows); output bf16 or fp32.
+#include "kernels_inst.hpp"
+
+namespace mg {
+
+const KernelEntry *entries_bf16(int *n) {
+  static const KernelEntry table[] = {
+      make_entry<__bf16, __bf16, 256, 256, 64, 2, 2, true, true>("mfma_bf16_256x256x64_w2x2"),
+      make_entry<__bf16, __bf16, 256, 128, 64, 2, 2, true, true>("mfma_bf16_256x128x64_w2x2"),
+      make_entry<__bf16, __bf16, 128, 256, 64, 2, 2, true, true>("mfma_bf16_128x256x64_w2x2"),
+      make_entry<__bf16, __bf16, 128, 128, 64, 2, 2, true, true>("mfma_bf16_128x128x64_w2x2"),
+      make_entry<__bf16, __bf16, 64, 64, 64, 2, 2, true, true>("mfma_bf16_64x64x64_w2x2"),
+      make_entry<__bf16, __bf16, 128, 128, 64, 2, 2, false, true>("elemA_bf16_128x128x64_w2x2"),
+      make_entry<__bf16, __bf16, 128, 128, 64, 2, 2, true, false>("elemB_bf16_128x128x64_w2x2"),
+      make_entry<__bf16, __bf16, 128, 128, 64, 2, 2, false, false>("elemAB_bf16_128x128x64_w2x2"),
+  };
+  *n = (int)(sizeof(table) / sizeof(table[0]));
+  return table;
+}
+
+}  // namespace mg

@@ -1,0 +1,22 @@
+// f16-input GEMM configurations: v_mfma_f32_16x16x32_f16, fp32 accumulate,
+// BK = 64 (128-byte LDS rows); output f16 or fp32.
+#include "kernels_inst.hpp"
+
+namespace mg {
+
+const KernelEntry *entries_f16(int *n) {
+  static const KernelEntry table[] = {
+      make_entry<_Float16, _Float16, 256, 256, 64, 2, 2, true, true>("mfma_f16_256x256x64_w2x2"),
+      make_entry<_Float16, _Float16, 256, 128, 64, 2, 2, true, true>("mfma_f16_256x128x64_w2x2"),
+      make_entry<_Float16, _Float16, 128, 256, 64, 2, 2, true, true>("mfma_f16_128x256x64_w2x2"),
+      make_entry<_Float16, _Float16, 128, 128, 64, 2, 2, true, true>("mfma_f16_128x128x64_w2x2"),
+      make_entry<_Float16, _Float16, 64, 64, 64, 2, 2, true, true>("mfma_f16_64x64x64_w2x2"),
+      make_entry<_Float16, _Float16, 128, 128, 64, 2, 2, false, true>("elemA_f16_128x128x64_w2x2"),
+      make_entry<_Float16, _Float16, 128, 128, 64, 2, 2, true, false>("elemB_f16_128x128x64_w2x2"),
+      make_entry<_Float16, _Float16, 128, 128, 64, 2, 2, false, false>("elemAB_f16_128x128x64_w2x2"),
+  };
+  *n = (int)(sizeof(table) / sizeof(table[0]));
+  return table;
+}
+
+}  // namespace mg

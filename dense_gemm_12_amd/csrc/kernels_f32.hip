@@ -1,0 +1,38 @@
+// fp32 SGEMM configurations: v_mfma_f32_16x16x4_f32, BK = 32 (128-byte LDS rows).
+#include "kernels_inst.hpp"
+
+namespace mg {
+
+const KernelEntry *entries_f32(int *n) {
+  static const KernelEntry table[] = {
+      make_entry<float, float, 128, 128, 32, 2, 2, true, true>("mfma_f32_128x128x32_w2x2"),
+      make_entry<float, float, 256, 128, 32, 2, 2, true, true>("mfma_f32_256x128x32_w2x2"),
+      make_entry<float, float, 128, 256, 32, 2, 2, true, true>("mfma_f32_128x256x32_w2x2"),
+      make_entry<float, float, 256, 256, 32, 2, 2, true, true>("mfma_f32_256x256x32_w2x2"),
+      make_entry<float, float, 64, 64, 32, 2, 2, true, true>("mfma_f32_64x64x32_w2x2"),
+      make_entry<float, float, 128, 128, 32, 2, 2, false, true>("elemA_f32_128x128x32_w2x2"),
+      make_entry<float, float, 128, 128, 32, 2, 2, true, false>("elemB_f32_128x128x32_w2x2"),
+      make_entry<float, float, 128, 128, 32, 2, 2, false, false>("elemAB_f32_128x128x32_w2x2"),
+  };
+  *n = (int)(sizeof(table) / sizeof(table[0]));
+  return table;
+}
+
+template <typename TO>
+static hipError_t launch_scale(const GemmParams &p, hipStream_t s) {
+  const int64_t total = (int64_t)p.M * p.N;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(scale_c_kernel<TO>, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+LaunchFn scale_launcher(int c_dtype) {
+  switch (c_dtype) {
+    case 0: return &launch_scale<float>;
+    case 1: return &launch_scale<_Float16>;
+    default: return &launch_scale<__bf16>;
+  }
+}
+
+}  // namespace mg

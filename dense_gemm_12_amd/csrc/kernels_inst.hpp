@@ -1,0 +1,45 @@
+// Instantiation helpers: expand one tile configuration over the four storage
+// layouts and the output types of an input type.
+#pragma once
+#include "gemm_kernel.hpp"
+
+namespace mg {
+
+template <class Tile>
+hipError_t launch_tile(const GemmParams &p, hipStream_t s) {
+  hipLaunchKernelGGL(gemm_kernel<Tile>, dim3(p.tiles_m * p.tiles_n), dim3(Tile::NT), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename TI, typename TO, int BM, int BN, int BK, int WM, int WN, bool AV, bool BV>
+struct LayoutSet {
+  template <bool AKC, bool BKC>
+  using T = GemmTile<TI, TO, BM, BN, BK, WM, WN, AKC, BKC, AV, BV>;
+  static void fill(LaunchFn (&f)[2][2]) {
+    f[0][0] = &launch_tile<T<false, false>>;
+    f[0][1] = &launch_tile<T<false, true>>;
+    f[1][0] = &launch_tile<T<true, false>>;
+    f[1][1] = &launch_tile<T<true, true>>;
+  }
+};
+
+// TI: input type; TO16: the 16-bit output type (ignored for fp32 inputs).
+template <typename TI, typename TO16, int BM, int BN, int BK, int WM, int WN, bool AV, bool BV>
+KernelEntry make_entry(const char *name) {
+  KernelEntry e{};
+  e.name = name;
+  e.bm = BM;
+  e.bn = BN;
+  e.bk = BK;
+  e.a_vec = AV;
+  e.b_vec = BV;
+  LayoutSet<TI, float, BM, BN, BK, WM, WN, AV, BV>::fill(e.fn[1]);
+  if constexpr (sizeof(TI) == 4) {
+    LayoutSet<TI, float, BM, BN, BK, WM, WN, AV, BV>::fill(e.fn[0]);
+  } else {
+    LayoutSet<TI, TO16, BM, BN, BK, WM, WN, AV, BV>::fill(e.fn[0]);
+  }
+  return e;
+}
+
+}  // namespace mg

@@ -1,0 +1,369 @@
+// The C ABI of libmgemm (declared in include/mgemm.h): argument validation,
+// the shape-keyed planner (tuning table + built-in heuristic) and the launch
+// on the caller's stream.  No allocation, no printing, no exceptions across
+// the boundary.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/mgemm.h"
+#include "gemm_params.hpp"
+
+using mg::GemmParams;
+using mg::KernelEntry;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;  // dimensions must be < 2^31
+constexpr int64_t kMaxLd = (int64_t)1 << 21;   // per-slice byte offsets stay below 2^31
+
+int elem_size(int dtype) { return dtype == MG_F32 ? 4 : 2; }
+
+const KernelEntry *entries(int in_type, int *n) {
+  switch (in_type) {
+    case MG_F32: return mg::entries_f32(n);
+    case MG_F16: return mg::entries_f16(n);
+    case MG_BF16: return mg::entries_bf16(n);
+    default: *n = 0; return nullptr;
+  }
+}
+
+// ----------------------------------------------------------- tuning table --
+struct Rule {
+  int in, c, ta, tb;
+  int64_t M, N, K;
+  std::string config;
+};
+std::vector<Rule> g_rules;  // read-only after mg_load_tune_table
+
+int find_config(int in_type, const char *name) {
+  int n = 0;
+  const KernelEntry *e = entries(in_type, &n);
+  for (int i = 0; i < n; ++i)
+    if (strcmp(e[i].name, name) == 0) return i;
+  return -1;
+}
+
+int parse_dtype(const char *s) {
+  if (!strcmp(s, "f32")) return MG_F32;
+  if (!strcmp(s, "f16")) return MG_F16;
+  if (!strcmp(s, "bf16")) return MG_BF16;
+  return -1;
+}
+
+// ----------------------------------------------------------- validation --
+struct Problem {
+  int in_type, c_type, ta, tb;
+  int64_t M, N, K, lda, ldb, ldc;
+  float alpha, beta;
+  const void *A, *B;
+  void *C;
+};
+
+bool ranges_overlap(const void *p, int64_t pbytes, const void *q, int64_t qbytes) {
+  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+  return a < b + (uintptr_t)qbytes && b < a + (uintptr_t)pbytes;
+}
+
+// Bytes spanned by a stored rows x cols row-major matrix with leading dim ld.
+int64_t span_bytes(int64_t rows, int64_t cols, int64_t ld, int es) {
+  if (rows <= 0 || cols <= 0) return 0;
+  return ((rows - 1) * ld + cols) * es;
+}
+
+mg_status validate(const Problem &p) {
+  if (p.ta != MG_N && p.ta != MG_T) return MG_EINVAL;
+  if (p.tb != MG_N && p.tb != MG_T) return MG_EINVAL;
+  if (p.in_type == MG_F32 && p.c_type != MG_F32) return MG_EINVAL;
+  if (p.in_type == MG_F16 && p.c_type != MG_F16 && p.c_type != MG_F32) return MG_EINVAL;
+  if (p.in_type == MG_BF16 && p.c_type != MG_BF16 && p.c_type != MG_F32) return MG_EINVAL;
+  if (p.M < 0 || p.N < 0 || p.K < 0) return MG_EINVAL;
+  // stored shapes
+  const int64_t a_rows = p.ta == MG_N ? p.M : p.K, a_cols = p.ta == MG_N ? p.K : p.M;
+  const int64_t b_rows = p.tb == MG_N ? p.K : p.N, b_cols = p.tb == MG_N ? p.N : p.K;
+  const int64_t one = 1;
+  if (p.lda < (a_cols > one ? a_cols : one)) return MG_EINVAL;
+  if (p.ldb < (b_cols > one ? b_cols : one)) return MG_EINVAL;
+  if (p.ldc < (p.N > one ? p.N : one)) return MG_EINVAL;
+  if (p.M == 0 || p.N == 0) return MG_OK;
+  if (p.C == nullptr) return MG_EINVAL;
+  const bool reads_ab = p.K > 0 && p.alpha != 0.0f;
+  if (reads_ab && (p.A == nullptr || p.B == nullptr)) return MG_EINVAL;
+  const int es = elem_size(p.in_type), ces = elem_size(p.c_type);
+  const int64_t c_bytes = span_bytes(p.M, p.N, p.ldc, ces);
+  if (reads_ab) {
+    if (ranges_overlap(p.C, c_bytes, p.A, span_bytes(a_rows, a_cols, p.lda, es))) return MG_EINVAL;
+    if (ranges_overlap(p.C, c_bytes, p.B, span_bytes(b_rows, b_cols, p.ldb, es))) return MG_EINVAL;
+  }
+  if (p.M >= kMaxDim || p.N >= kMaxDim || p.K >= kMaxDim) return MG_EUNSUPPORTED;
+  if (p.ldc >= kMaxDim) return MG_EUNSUPPORTED;
+  if (reads_ab && (p.lda > kMaxLd || p.ldb > kMaxLd)) return MG_EUNSUPPORTED;
+  if ((p.M + 15) / 16 * ((p.N + 15) / 16) >= kMaxDim) return MG_EUNSUPPORTED;
+  return MG_OK;
+}
+
+// 16-byte loads along an operand's contiguous dimension are legal.
+bool vec_ok(const void *base, int64_t ld, int64_t contiguous_extent, int es) {
+  const int v = 16 / es;
+  return ((uintptr_t)base % 16 == 0) && ((ld * es) % 16 == 0) && (contiguous_extent % v == 0);
+}
+
+// ------------------------------------------------------------- planning --
+struct Plan {
+  int config;
+  bool a_vec, b_vec;
+};
+
+int64_t tiles_for(int64_t M, int64_t N, int bm, int bn) {
+  return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+}
+
+// Built-in choice among the fully vectorised configurations: the largest
+// tile that still gives at least one wave of workgroups per CU (256 CUs),
+// else the tile with the most workgroups.
+int heuristic_config(int in_type, int64_t M, int64_t N) {
+  int n = 0;
+  const KernelEntry *e = entries(in_type, &n);
+  int best = -1;
+  int64_t best_area = -1;
+  for (int i = 0; i < n; ++i) {
+    if (!e[i].a_vec || !e[i].b_vec) continue;
+    const int64_t t = tiles_for(M, N, e[i].bm, e[i].bn);
+    const int64_t area = (int64_t)e[i].bm * e[i].bn;
+    if (t >= 256 && area > best_area) {
+      best = i;
+      best_area = area;
+    }
+  }
+  if (best >= 0) return best;
+  int64_t most = -1;
+  for (int i = 0; i < n; ++i) {
+    if (!e[i].a_vec || !e[i].b_vec) continue;
+    const int64_t t = tiles_for(M, N, e[i].bm, e[i].bn);
+    if (t > most || (t == most && best >= 0 &&
+                     (int64_t)e[i].bm * e[i].bn > (int64_t)e[best].bm * e[best].bn)) {
+      most = t;
+      best = i;
+    }
+  }
+  return best;
+}
+
+int table_config(const Problem &p) {
+  const Rule *best = nullptr;
+  double best_d = 1e300;
+  for (const Rule &r : g_rules) {
+    if (r.in != p.in_type || r.c != p.c_type || r.ta != p.ta || r.tb != p.tb) continue;
+    const double d = fabs(log2((double)(p.M + 1) / (r.M + 1))) +
+                     fabs(log2((double)(p.N + 1) / (r.N + 1))) +
+                     fabs(log2((double)(p.K + 1) / (r.K + 1)));
+    if (d < best_d) {
+      best_d = d;
+      best = &r;
+    }
+  }
+  if (!best || best_d > 1.5) return -1;  // only near neighbours are trusted
+  return find_config(p.in_type, best->config.c_str());
+}
+
+// The fallback configuration matching the operands' vector legality.
+int elem_config(int in_type, bool a_vec, bool b_vec) {
+  int n = 0;
+  const KernelEntry *e = entries(in_type, &n);
+  for (int i = 0; i < n; ++i)
+    if (e[i].a_vec == a_vec && e[i].b_vec == b_vec && !(a_vec && b_vec)) return i;
+  return -1;
+}
+
+Plan plan(const Problem &p) {
+  const int es = elem_size(p.in_type);
+  const bool a_kc = p.ta == MG_N, b_kc = p.tb == MG_T;
+  Plan pl;
+  pl.a_vec = vec_ok(p.A, p.lda, a_kc ? p.K : p.M, es);
+  pl.b_vec = vec_ok(p.B, p.ldb, b_kc ? p.K : p.N, es);
+  if (pl.a_vec && pl.b_vec) {
+    int c = table_config(p);
+    pl.config = c >= 0 ? c : heuristic_config(p.in_type, p.M, p.N);
+  } else {
+    pl.config = elem_config(p.in_type, pl.a_vec, pl.b_vec);
+  }
+  return pl;
+}
+
+}  // namespace
+
+// Implementation shared by the entry points.
+static mg_status run(const Problem &p, int forced, void *stream_v) {
+  mg_status s = validate(p);
+  if (s != MG_OK) return s;
+  if (p.M == 0 || p.N == 0) return MG_OK;
+  int n = 0;
+  const KernelEntry *e = entries(p.in_type, &n);
+  if (forced < -1 || forced >= n) return MG_EINVAL;
+  hipStream_t stream = static_cast<hipStream_t>(stream_v);
+
+  GemmParams gp{};
+  gp.A = p.A;
+  gp.B = p.B;
+  gp.C = p.C;
+  gp.lda = p.lda;
+  gp.ldb = p.ldb;
+  gp.ldc = p.ldc;
+  gp.M = (int)p.M;
+  gp.N = (int)p.N;
+  gp.K = (int)p.K;
+  gp.alpha = p.alpha;
+  gp.beta = p.beta;
+  const int ces = elem_size(p.c_type);
+  gp.c_vec = ((uintptr_t)p.C % (ces == 4 ? 16 : 8) == 0) && (p.ldc % 4 == 0);
+  const int c_idx = p.c_type == MG_F32 ? 0 : (p.c_type == MG_F16 ? 1 : 2);
+
+  hipError_t err;
+  if (p.K == 0 || p.alpha == 0.0f) {
+    err = mg::scale_launcher(c_idx)(gp, stream);
+  } else {
+    Plan pl = plan(p);
+    int cfg = forced >= 0 ? forced : pl.config;
+    if (cfg < 0) return MG_EUNSUPPORTED;
+    const KernelEntry &k = e[cfg];
+    if ((k.a_vec && !pl.a_vec) || (k.b_vec && !pl.b_vec)) return MG_EUNSUPPORTED;
+    gp.tiles_m = (int)((p.M + k.bm - 1) / k.bm);
+    gp.tiles_n = (int)((p.N + k.bn - 1) / k.bn);
+    gp.group_m = 8;
+    const int c_is_f32 = (p.c_type == MG_F32) ? 1 : 0;
+    const int a_kc = p.ta == MG_N ? 1 : 0, b_kc = p.tb == MG_T ? 1 : 0;
+    err = k.fn[c_is_f32][a_kc][b_kc](gp, stream);
+  }
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    return MG_EHIP;
+  }
+  return MG_OK;
+}
+
+extern "C" {
+
+mg_status gemm_f32_cfg(int config, mg_op ta, mg_op tb, int64_t M, int64_t N, int64_t K,
+                       float alpha, const float *A, int64_t lda, const float *B, int64_t ldb,
+                       float beta, float *C, int64_t ldc, void *stream) {
+  Problem p{MG_F32, MG_F32, (int)ta, (int)tb, M, N, K, lda, ldb, ldc, alpha, beta, A, B, C};
+  return run(p, config, stream);
+}
+
+mg_status gemm_f16_cfg(int config, mg_op ta, mg_op tb, int64_t M, int64_t N, int64_t K,
+                       float alpha, const uint16_t *A, int64_t lda, const uint16_t *B,
+                       int64_t ldb, float beta, void *C, mg_dtype c_type, int64_t ldc,
+                       void *stream) {
+  Problem p{MG_F16, (int)c_type, (int)ta, (int)tb, M, N, K, lda, ldb, ldc, alpha, beta, A, B, C};
+  return run(p, config, stream);
+}
+
+mg_status gemm_bf16_cfg(int config, mg_op ta, mg_op tb, int64_t M, int64_t N, int64_t K,
+                        float alpha, const uint16_t *A, int64_t lda, const uint16_t *B,
+                        int64_t ldb, float beta, void *C, mg_dtype c_type, int64_t ldc,
+                        void *stream) {
+  Problem p{MG_BF16, (int)c_type, (int)ta, (int)tb, M, N, K, lda, ldb, ldc, alpha, beta, A, B, C};
+  return run(p, config, stream);
+}
+
+mg_status gemm_f32(mg_op ta, mg_op tb, int64_t M, int64_t N, int64_t K, float alpha,
+                   const float *A, int64_t lda, const float *B, int64_t ldb, float beta, float *C,
+                   int64_t ldc, void *stream) {
+  return gemm_f32_cfg(-1, ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+mg_status gemm_f16(mg_op ta, mg_op tb, int64_t M, int64_t N, int64_t K, float alpha,
+                   const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, float beta,
+                   void *C, mg_dtype c_type, int64_t ldc, void *stream) {
+  return gemm_f16_cfg(-1, ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream);
+}
+
+mg_status gemm_bf16(mg_op ta, mg_op tb, int64_t M, int64_t N, int64_t K, float alpha,
+                    const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, float beta,
+                    void *C, mg_dtype c_type, int64_t ldc, void *stream) {
+  return gemm_bf16_cfg(-1, ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream);
+}
+
+int mg_num_configs(mg_dtype in_type) {
+  int n = 0;
+  entries((int)in_type, &n);
+  return n;
+}
+
+const char *mg_config_name(mg_dtype in_type, int config) {
+  int n = 0;
+  const KernelEntry *e = entries((int)in_type, &n);
+  if (config < 0 || config >= n) return nullptr;
+  return e[config].name;
+}
+
+int mg_chosen_config(mg_dtype in_type, mg_dtype c_type, mg_op ta, mg_op tb, int64_t M, int64_t N,
+                     int64_t K) {
+  // Planned as for 16-byte-aligned operands with contiguous leading dimensions.
+  const int64_t lda = ta == MG_N ? K : M, ldb = tb == MG_N ? N : K;
+  Problem p{(int)in_type, (int)c_type, (int)ta, (int)tb, M, N, K, lda, ldb, N, 1.0f, 0.0f,
+            (const void *)(uintptr_t)4096, (const void *)(uintptr_t)4096, nullptr};
+  if (M <= 0 || N <= 0 || K <= 0) return -1;
+  return plan(p).config;
+}
+
+mg_status mg_load_tune_table(const char *path) {
+  if (!path) return MG_EINVAL;
+  FILE *f = fopen(path, "r");
+  if (!f) return MG_EINVAL;
+  std::vector<Rule> rules;
+  char line[512];
+  bool ok = true;
+  while (fgets(line, sizeof line, f)) {
+    if (line[0] == '#' || line[0] == '\n' || line[0] == '\0') continue;
+    char in[16], c[16], ta[4], tb[4], cfg[128];
+    long long M, N, K;
+    if (sscanf(line, "%15s %15s %3s %3s %lld %lld %lld %127s", in, c, ta, tb, &M, &N, &K, cfg) != 8) {
+      ok = false;
+      break;
+    }
+    Rule r;
+    r.in = parse_dtype(in);
+    r.c = parse_dtype(c);
+    r.ta = !strcmp(ta, "N") ? MG_N : (!strcmp(ta, "T") ? MG_T : -1);
+    r.tb = !strcmp(tb, "N") ? MG_N : (!strcmp(tb, "T") ? MG_T : -1);
+    r.M = M;
+    r.N = N;
+    r.K = K;
+    r.config = cfg;
+    if (r.in < 0 || r.c < 0 || r.ta < 0 || r.tb < 0 || find_config(r.in, cfg) < 0) {
+      ok = false;
+      break;
+    }
+    rules.push_back(r);
+  }
+  fclose(f);
+  if (!ok) return MG_EINVAL;
+  g_rules.swap(rules);
+  return MG_OK;
+}
+
+int mg_tune_table_size(void) { return (int)g_rules.size(); }
+
+const char *mg_status_str(mg_status s) {
+  switch (s) {
+    case MG_OK: return "ok";
+    case MG_EINVAL: return "invalid argument";
+    case MG_EUNSUPPORTED: return "unsupported problem (outside the kernels' addressing range)";
+    case MG_EHIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int mg_last_hip_error(void) { return g_last_hip_error; }
+
+const char *mg_version(void) { return "mgemm 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -66,3 +66,44 @@ def as_numpy_bits(t: torch.Tensor):
     if t.dtype == torch.float64:
         return t.numpy()
     raise TypeError(t.dtype)
+
+
+# ---- the named workloads (shapes, layouts, scalars and input recipes) ----------
+# ta/tb: False = op(X) is the stored matrix, True = its transpose.  "TN" (A
+# stored M x K, B stored N x K) is ta=False, tb=True.
+WORKLOADS = {
+    "fp32_nn_256": dict(wid=1, in_dtype="f32", c_dtype="f32", M=256, N=256, K=256, ta=False,
+                        tb=False, alpha=1.0, beta=0.0, dist="uniform"),
+    "fp32_nn_4092": dict(wid=2, in_dtype="f32", c_dtype="f32", M=4092, N=4092, K=4092, ta=False,
+                         tb=False, alpha=1.5, beta=0.5, dist="uniform"),
+    "fp32_nn_8192x8192x4096": dict(wid=3, in_dtype="f32", c_dtype="f32", M=8192, N=8192, K=4096,
+                                   ta=False, tb=False, alpha=1.0, beta=0.0, dist="normal"),
+    **{f"fp16_tn_{n}": dict(wid=4, in_dtype="f16", c_dtype="f16", M=n, N=n, K=n, ta=False,
+                            tb=True, alpha=1.0, beta=0.0, dist="normal_k")
+       for n in (2048, 4096, 8192, 16384)},
+    "bf16_nn_4096x11008x4096": dict(wid=5, in_dtype="bf16", c_dtype="f32", M=4096, N=11008,
+                                    K=4096, ta=False, tb=False, alpha=1.0, beta=1.0,
+                                    dist="uniform"),
+    "bf16_nn_127x4096x4095": dict(wid=5, in_dtype="bf16", c_dtype="f32", M=127, N=4096, K=4095,
+                                  ta=False, tb=False, alpha=1.0, beta=1.0, dist="uniform"),
+}
+
+
+def workload_inputs(name: str, integer_twin: bool = False):
+    """(A, B, C_in) CPU tensors of a named workload; C_in is None when beta == 0.
+
+    A is stored M x K (K x M if ta), B stored K x N (N x K if tb); C_in is
+    M x N in the output dtype.  The integer twin draws every matrix from
+    {-2..2} with seeds offset by 100."""
+    w = WORKLOADS[name]
+    M, N, K = w["M"], w["N"], w["K"]
+    sa = (K, M) if w["ta"] else (M, K)
+    sb = (N, K) if w["tb"] else (K, N)
+    dist = "int2" if integer_twin else w["dist"]
+    A = draw(*sa, dist, seed_for(w["wid"], "A", integer_twin), w["in_dtype"], scale_k=K)
+    B = draw(*sb, dist, seed_for(w["wid"], "B", integer_twin), w["in_dtype"], scale_k=K)
+    C = None
+    if w["beta"] != 0.0:
+        cdist = "int2" if integer_twin else "uniform"
+        C = draw(M, N, cdist, seed_for(w["wid"], "C", integer_twin), w["c_dtype"])
+    return A, B, C

@@ -1,0 +1,128 @@
+/*
+ * mgemm.h -- dense GEMM for AMD MI355X (gfx950): C = alpha * op(A) * op(B) + beta * C.
+ *
+ * The operation is the one the GEMM pages define: "SGEMM CUDA代码学习" (leetCUDA
+ * 15-sgemm), section 问题定义与记号 (C[m][n] = sum_k A[m][k] * B[k][n], row-major),
+ * with the alpha/beta update of "CUDA GEMM：从基础写法到工程优化" (opening
+ * definition) and of the worklog "如何优化一个 CUDA Matmul Kernel", Kernel 1.  The
+ * "TN" layout of "HGEMM SMEM Swizzle 代码学习" (kernel comment) and of "Warp
+ * Specialization HGEMM" section 6 (A row-major M x K, B stored N x K) is
+ * (ta = MG_N, tb = MG_T) here.
+ *
+ * Storage.  Every matrix is row-major: element (r, c) of a stored matrix X is
+ * at X + r * ldx + c (in elements).
+ *   op(A) is M x K: stored M x K (lda >= K) when ta == MG_N,
+ *                   stored K x M (lda >= M) when ta == MG_T.
+ *   op(B) is K x N: stored K x N (ldb >= N) when tb == MG_N,
+ *                   stored N x K (ldb >= K) when tb == MG_T.
+ *   C is M x N with ldc >= N; it is read (when beta != 0) and written.
+ *
+ * Arithmetic.  Products and sums are fp32 (fp16/bf16 inputs are multiplied
+ * exactly and accumulated in fp32); the epilogue computes alpha*acc + beta*C
+ * in fp32 and rounds once (nearest-even) to the C type.  Summation order is
+ * unspecified.  No TF32-style input rounding, no fast-math.
+ *
+ * Special cases (BLAS conventions):
+ *   M == 0 or N == 0       no-op, nothing is read or written.
+ *   K == 0 or alpha == 0   C = beta * C; A and B are not read.
+ *   beta == 0              C is write-only: C's old contents (even NaN) are
+ *                          never read.
+ *
+ * Pointers and ownership.  A, B, C are device pointers (HBM) owned by the
+ * caller; the library never allocates, frees or retains them, never writes
+ * A or B, and needs only element alignment (16-byte alignment of pointers and
+ * leading dimensions selects faster load/store paths).  C must not overlap A
+ * or B.  The call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ * stream): device-side faults appear at the caller's next synchronisation.
+ *
+ * Errors.  Every argument is validated before anything is launched; on an
+ * error C is untouched and the status says why:
+ *   MG_EINVAL        negative dimension, leading dimension too small, NULL
+ *                    pointer with a non-empty extent, unknown enum value,
+ *                    C overlapping A or B.
+ *   MG_EUNSUPPORTED  valid but outside what the kernels address: a dimension
+ *                    >= 2^31, or a leading dimension above 2^21 elements.
+ *   MG_EHIP          the launch failed; mg_last_hip_error() gives the code.
+ * Functions never throw and never print.  Calls are reentrant; the tuning
+ * table (mg_load_tune_table) is read-only once loaded.
+ */
+#ifndef MGEMM_H
+#define MGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MG_OK = 0, MG_EINVAL = 1, MG_EUNSUPPORTED = 2, MG_EHIP = 3 } mg_status;
+typedef enum { MG_N = 0, MG_T = 1 } mg_op;
+typedef enum { MG_F32 = 0, MG_F16 = 1, MG_BF16 = 2 } mg_dtype;
+
+/* fp32 SGEMM.  A, B, C are fp32. */
+mg_status gemm_f32(mg_op ta, mg_op tb, int64_t M, int64_t N, int64_t K, float alpha,
+                   const float *A, int64_t lda, const float *B, int64_t ldb, float beta,
+                   float *C, int64_t ldc, void *stream);
+
+/* fp16-input GEMM with fp32 accumulation.  A, B hold IEEE binary16 bit
+ * patterns; C is fp16 (c_type = MG_F16) or fp32 (c_type = MG_F32). */
+mg_status gemm_f16(mg_op ta, mg_op tb, int64_t M, int64_t N, int64_t K, float alpha,
+                   const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, float beta,
+                   void *C, mg_dtype c_type, int64_t ldc, void *stream);
+
+/* bf16-input GEMM with fp32 accumulation.  A, B hold bfloat16 bit patterns;
+ * C is bf16 (c_type = MG_BF16) or fp32 (c_type = MG_F32). */
+mg_status gemm_bf16(mg_op ta, mg_op tb, int64_t M, int64_t N, int64_t K, float alpha,
+                    const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, float beta,
+                    void *C, mg_dtype c_type, int64_t ldc, void *stream);
+
+/* The same three operations with the kernel configuration forced: `config`
+ * is an id in [0, mg_num_configs(in_type)) or -1 for the planner's choice.
+ * A configuration that cannot run the given problem (e.g. a fast-path
+ * variant on misaligned data) returns MG_EUNSUPPORTED.  Used by the
+ * autotuner and the profiling harness. */
+mg_status gemm_f32_cfg(int config, mg_op ta, mg_op tb, int64_t M, int64_t N, int64_t K,
+                       float alpha, const float *A, int64_t lda, const float *B, int64_t ldb,
+                       float beta, float *C, int64_t ldc, void *stream);
+mg_status gemm_f16_cfg(int config, mg_op ta, mg_op tb, int64_t M, int64_t N, int64_t K,
+                       float alpha, const uint16_t *A, int64_t lda, const uint16_t *B,
+                       int64_t ldb, float beta, void *C, mg_dtype c_type, int64_t ldc,
+                       void *stream);
+mg_status gemm_bf16_cfg(int config, mg_op ta, mg_op tb, int64_t M, int64_t N, int64_t K,
+                        float alpha, const uint16_t *A, int64_t lda, const uint16_t *B,
+                        int64_t ldb, float beta, void *C, mg_dtype c_type, int64_t ldc,
+                        void *stream);
+
+/* Kernel configurations available for an input type, and their names
+ * (static strings, e.g. "mfma_256x256x64_w2x2"). */
+int mg_num_configs(mg_dtype in_type);
+const char *mg_config_name(mg_dtype in_type, int config);
+
+/* The configuration the planner picks for a problem (or -1 if none fits). */
+int mg_chosen_config(mg_dtype in_type, mg_dtype c_type, mg_op ta, mg_op tb, int64_t M, int64_t N,
+                     int64_t K);
+
+/* Load a shape-keyed tuning table (text, one rule per line:
+ * "<in> <c> <ta> <tb> <M> <N> <K> <config-name>", e.g. "f16 f16 N T 4096 4096 4096
+ * mfma_256x256x64_w2x2"); lines starting with '#' are comments.  Exact shape
+ * matches win; otherwise the nearest rule of the same type/layout class by
+ * log-distance of M, N, K.  Replaces any table loaded before.  Returns
+ * MG_EINVAL if the file cannot be read or a line names an unknown config
+ * (the previous table is then kept).  Not safe to call concurrently with
+ * GEMM calls. */
+mg_status mg_load_tune_table(const char *path);
+/* Number of rules in the loaded table (0 if none). */
+int mg_tune_table_size(void);
+
+/* Human-readable status text (static string). */
+const char *mg_status_str(mg_status s);
+/* The hipError_t of the most recent MG_EHIP on the calling thread (0 if none). */
+int mg_last_hip_error(void);
+/* Library version string. */
+const char *mg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MGEMM_H */

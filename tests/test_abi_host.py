@@ -1,0 +1,172 @@
+"""Host-only checks of the C ABI (no GPU needed, no kernel launched).
+
+Every call made here is rejected or finished by the host-side validation
+before anything reaches HIP: invalid arguments, or empty problems.
+"""
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mgemm.h")
+
+
+@pytest.fixture(scope="module")
+def mg():
+    import dense_gemm_12_amd as mg
+    if not os.path.exists(mg.LIB_PATH):
+        from dense_gemm_12_amd import build
+        build.build()
+    mg.load()
+    return mg
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported(mg):
+    names = declared_functions()
+    assert len(names) >= 14
+    assert sorted(names) == sorted(mg.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", mg.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(mg.load(), n)
+
+
+def test_version_and_status_strings(mg):
+    lib = mg.load()
+    assert b"gfx950" in lib.mg_version()
+    for s in range(4):
+        assert lib.mg_status_str(s)
+    assert lib.mg_last_hip_error() == 0
+
+
+FAKE_A, FAKE_B, FAKE_C = 1 << 20, 1 << 40, 1 << 46  # never dereferenced
+
+
+def call(mg, fn="gemm_f32", ta=0, tb=0, M=4, N=4, K=4, alpha=1.0, A=FAKE_A, lda=None, B=FAKE_B,
+         ldb=None, beta=0.0, C=FAKE_C, ldc=None, c_type=None, config=None):
+    lda = lda if lda is not None else (K if ta == 0 else M)
+    ldb = ldb if ldb is not None else (N if tb == 0 else K)
+    ldc = ldc if ldc is not None else N
+    lib = mg.load()
+    args = [ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C]
+    if fn != "gemm_f32":
+        args.append(c_type if c_type is not None else (mg.MG_F16 if fn == "gemm_f16" else mg.MG_BF16))
+    args += [ldc, None]
+    if config is not None:
+        return getattr(lib, fn + "_cfg")(config, *args)
+    return getattr(lib, fn)(*args)
+
+
+@pytest.mark.parametrize("fn", ["gemm_f32", "gemm_f16", "gemm_bf16"])
+def test_invalid_arguments_are_rejected_before_launch(mg, fn):
+    E = mg.MG_EINVAL
+    assert call(mg, fn, M=-1) == E
+    assert call(mg, fn, N=-1) == E
+    assert call(mg, fn, K=-1) == E
+    assert call(mg, fn, ta=2) == E
+    assert call(mg, fn, tb=-1) == E
+    assert call(mg, fn, lda=3) == E                 # lda < K (A stored M x K)
+    assert call(mg, fn, ta=1, M=8, lda=7) == E       # lda < M (A stored K x M)
+    assert call(mg, fn, ldb=3) == E                 # ldb < N
+    assert call(mg, fn, tb=1, K=9, ldb=8) == E       # ldb < K (B stored N x K)
+    assert call(mg, fn, ldc=3) == E
+    assert call(mg, fn, C=0) == E
+    assert call(mg, fn, A=0) == E
+    assert call(mg, fn, B=0) == E
+    # C overlapping A or B
+    assert call(mg, fn, C=FAKE_A + 8) == E
+    assert call(mg, fn, B=FAKE_C + 4) == E
+    # forced configuration out of range
+    assert call(mg, fn, config=10 ** 6) == E
+    assert call(mg, fn, config=-2) == E
+
+
+def test_output_type_must_match_input_type(mg):
+    E = mg.MG_EINVAL
+    assert call(mg, "gemm_f16", c_type=mg.MG_BF16) == E
+    assert call(mg, "gemm_bf16", c_type=mg.MG_F16) == E
+    assert call(mg, "gemm_f16", c_type=7) == E
+
+
+def test_unsupported_ranges(mg):
+    U = mg.MG_EUNSUPPORTED
+    assert call(mg, M=1 << 31, K=4, lda=4) == U
+    assert call(mg, K=1 << 22, lda=1 << 22, tb=0, ldb=4) == U  # lda above 2^21 elements
+
+
+def test_empty_problems_finish_on_the_host(mg):
+    OK = mg.MG_OK
+    # M == 0 or N == 0: nothing is read or written, NULL pointers allowed
+    assert call(mg, M=0, A=0, B=0, C=0) == OK
+    assert call(mg, "gemm_f16", N=0, ldb=1, ldc=1, A=0, B=0, C=0) == OK
+    assert call(mg, "gemm_bf16", M=0, N=0, K=0, lda=1, ldb=1, ldc=1, A=0, B=0, C=0) == OK
+    # leading dimensions are still at least 1 (BLAS convention)
+    assert call(mg, "gemm_f16", N=0, ldb=0, ldc=1, A=0, B=0, C=0) == mg.MG_EINVAL
+
+
+def test_configs_are_listed_and_named(mg):
+    for t in ("f32", "f16", "bf16"):
+        n = mg.num_configs(t)
+        assert n >= 4
+        names = [mg.config_name(t, i) for i in range(n)]
+        assert len(set(names)) == n
+        assert mg.config_name(t, n) is None
+        assert all(t in nm for nm in names)
+
+
+def test_planner_prefers_big_tiles_for_big_problems(mg):
+    big = mg.chosen_config("f16", "f16", 0, 1, 8192, 8192, 8192)
+    small = mg.chosen_config("f16", "f16", 0, 1, 512, 512, 512)
+    nb = mg.config_name("f16", big)
+    ns = mg.config_name("f16", small)
+    area = lambda n: int(re.search(r"_(\d+)x(\d+)x", n).group(1)) * int(re.search(r"_(\d+)x(\d+)x", n).group(2))
+    assert area(nb) > area(ns)
+    assert mg.chosen_config("f32", "f32", 0, 0, 0, 4, 4) == -1
+
+
+def test_tune_table_load_and_reject(mg, tmp_path):
+    good = tmp_path / "t.txt"
+    name = mg.config_name("f16", 3)
+    good.write_text(f"# comment\nf16 f16 N T 4096 4096 4096 {name}\n")
+    mg.load_tune_table(str(good))
+    assert mg.load().mg_tune_table_size() == 1
+    assert mg.chosen_config("f16", "f16", 0, 1, 4096, 4096, 4096) == 3
+    bad = tmp_path / "bad.txt"
+    bad.write_text("f16 f16 N T 4096 4096 4096 no_such_config\n")
+    with pytest.raises(mg.MgemmError):
+        mg.load_tune_table(str(bad))
+    assert mg.load().mg_tune_table_size() == 1  # previous table kept
+    with pytest.raises(mg.MgemmError):
+        mg.load_tune_table(str(tmp_path / "missing.txt"))
+    # restore the packaged table (or none)
+    empty = tmp_path / "empty.txt"
+    empty.write_text("")
+    mg.load_tune_table(mg.TUNE_TABLE if os.path.exists(mg.TUNE_TABLE) else str(empty))
+
+
+def test_product_path_has_no_oracle_or_cpu_fallback():
+    """The package never imports the oracle, and fails loudly without its library."""
+    pkg = os.path.join(ROOT, "dense_gemm_12_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "oracle_gemm" not in text, f
+    code = ("import dense_gemm_12_amd as mg\n"
+            "try:\n    mg.load('/nonexistent/libmgemm.so')\nexcept RuntimeError:\n    print('raised')\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
+    assert "raised" in out.stdout
