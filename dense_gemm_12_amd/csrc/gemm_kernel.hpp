@@ -24,6 +24,7 @@
 // single 16- or 8-byte write.
 #pragma once
 #include "gemm_params.hpp"
+#include "epilogue.hpp"
 #include "gfx950_prims.hpp"
 
 namespace mg {
@@ -265,68 +266,9 @@ struct GemmTile {
       __syncthreads();
     }
 
-    epilogue(p, acc, m0 + wm * WTM, n0 + wn * WTN, lane);
+    GemmEpilogue<TO, MI, NJ>::store(p, acc, m0 + wm * WTM, n0 + wn * WTN, lane);
   }
 
-  // C[m][n..n+3] for m = mw + i*16 + lane%16, n = nw + j*16 + 4*(lane/16).
-  static __device__ __forceinline__ void epilogue(const GemmParams &p, const f32x4 (&acc)[MI][NJ],
-                                                  int mw, int nw, int lane) {
-    TO *C = static_cast<TO *>(p.C);
-    const float alpha = p.alpha, beta = p.beta;
-    const bool use_beta = beta != 0.0f;
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const int m = mw + i * 16 + (lane & 15);
-      if (m >= p.M) continue;
-      TO *crow = C + (int64_t)m * p.ldc;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int n = nw + j * 16 + (lane >> 4) * 4;
-        if (n >= p.N) continue;
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = alpha * acc[i][j][e];
-        if (p.c_vec && n + 3 < p.N) {
-          if constexpr (sizeof(TO) == 4) {
-            f32x4 *cp = reinterpret_cast<f32x4 *>(crow + n);
-            if (use_beta) {
-              const f32x4 c = *cp;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] = fmaf(beta, c[e], v[e]);
-            }
-            *cp = f32x4{v[0], v[1], v[2], v[3]};
-          } else {
-            u32x2 *cp = reinterpret_cast<u32x2 *>(crow + n);
-            if (use_beta) {
-              const u32x2 c = *cp;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const uint16_t bits = (uint16_t)(c[e >> 1] >> (16 * (e & 1)));
-                v[e] = fmaf(beta, to_f32(__builtin_bit_cast(TO, bits)), v[e]);
-              }
-            }
-            u32x2 o;
-#pragma unroll
-            for (int d = 0; d < 2; ++d) {
-              const uint32_t lo = __builtin_bit_cast(uint16_t, from_f32<TO>(v[2 * d]));
-              const uint32_t hi = __builtin_bit_cast(uint16_t, from_f32<TO>(v[2 * d + 1]));
-              o[d] = lo | (hi << 16);
-            }
-            *cp = o;
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (n + e < p.N) {
-              float x = v[e];
-              if (use_beta) x = fmaf(beta, to_f32(crow[n + e]), x);
-              crow[n + e] = from_f32<TO>(x);
-            }
-          }
-        }
-      }
-    }
-  }
 };
 
 template <class Tile>
@@ -344,7 +286,9 @@ __global__ void __launch_bounds__(256) scale_c_kernel(GemmParams p) {
        idx += (int64_t)gridDim.x * blockDim.x) {
     const int64_t m = idx / p.N, n = idx - m * p.N;
     TO *c = C + m * p.ldc + n;
-    *c = from_f32<TO>(p.beta == 0.0f ? 0.0f : p.beta * to_f32(*c));
+    // alpha * (empty or ignored product) contributes +0: 0 + beta*C (so a
+    // -0 product beta*C becomes +0, as in the formula's left-to-right sum).
+    *c = from_f32<TO>(p.beta == 0.0f ? 0.0f : 0.0f + p.beta * to_f32(*c));
   }
 }
 

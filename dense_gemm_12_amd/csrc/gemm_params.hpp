@@ -21,12 +21,16 @@ struct GemmParams {
 typedef hipError_t (*LaunchFn)(const GemmParams &, hipStream_t);
 
 // One compiled tile configuration; fn[c_is_f32][a_kc][b_kc] covers the
-// output type and the four storage layouts.  a_vec / b_vec tell whether the
-// variant needs 16-byte-loadable operands.
+// output type and the four storage layouts (a_kc: A stored M x K; b_kc: B
+// stored N x K); a null entry means the layout is not supported by this
+// configuration.  a_vec / b_vec tell whether the variant needs
+// 16-byte-loadable operands.  kind: 0 = register-staged loads, 1 = direct
+// global->LDS loads.
 struct KernelEntry {
   const char *name;
   int bm, bn, bk;
   bool a_vec, b_vec;
+  int kind;
   LaunchFn fn[2][2][2];
 };
 

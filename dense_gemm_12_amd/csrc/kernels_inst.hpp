@@ -1,6 +1,7 @@
 // Instantiation helpers: expand one tile configuration over the four storage
 // layouts and the output types of an input type.
 #pragma once
+#include "gemm_dma_kernel.hpp"
 #include "gemm_kernel.hpp"
 
 namespace mg {
@@ -33,12 +34,36 @@ KernelEntry make_entry(const char *name) {
   e.bk = BK;
   e.a_vec = AV;
   e.b_vec = BV;
+  e.kind = 0;
   LayoutSet<TI, float, BM, BN, BK, WM, WN, AV, BV>::fill(e.fn[1]);
   if constexpr (sizeof(TI) == 4) {
     LayoutSet<TI, float, BM, BN, BK, WM, WN, AV, BV>::fill(e.fn[0]);
   } else {
     LayoutSet<TI, TO16, BM, BN, BK, WM, WN, AV, BV>::fill(e.fn[0]);
   }
+  return e;
+}
+
+template <class Tile>
+hipError_t launch_dma_tile(const GemmParams &p, hipStream_t s) {
+  hipLaunchKernelGGL(gemm_dma_kernel<Tile>, dim3(p.tiles_m * p.tiles_n), dim3(Tile::NT), 0, s, p);
+  return hipGetLastError();
+}
+
+// Direct-to-LDS configurations exist for the k-contiguous layout of both
+// operands only (A stored M x K, B stored N x K).
+template <typename TI, typename TO16, int BM, int BN, int BK, int ST, int WM, int WN>
+KernelEntry make_dma_entry(const char *name) {
+  KernelEntry e{};
+  e.name = name;
+  e.bm = BM;
+  e.bn = BN;
+  e.bk = BK;
+  e.a_vec = true;
+  e.b_vec = true;
+  e.kind = 1;
+  e.fn[1][1][1] = &launch_dma_tile<DmaTile<TI, float, BM, BN, BK, ST, WM, WN>>;
+  e.fn[0][1][1] = &launch_dma_tile<DmaTile<TI, TO16, BM, BN, BK, ST, WM, WN>>;
   return e;
 }
 

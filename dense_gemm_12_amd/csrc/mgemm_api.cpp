@@ -125,32 +125,26 @@ int64_t tiles_for(int64_t M, int64_t N, int bm, int bn) {
   return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
 }
 
-// Built-in choice among the fully vectorised configurations: the largest
-// tile that still gives at least one wave of workgroups per CU (256 CUs),
-// else the tile with the most workgroups.
-int heuristic_config(int in_type, int64_t M, int64_t N) {
+// Built-in choice among the fully vectorised configurations that support the
+// problem's layout: the largest tile that still gives at least one workgroup
+// per CU (256 CUs), else the tile with the most workgroups; direct-to-LDS
+// kernels win ties, then table order.
+int heuristic_config(const Problem &p) {
   int n = 0;
-  const KernelEntry *e = entries(in_type, &n);
+  const KernelEntry *e = entries(p.in_type, &n);
+  const int c = p.c_type == MG_F32 ? 1 : 0, akc = p.ta == MG_N, bkc = p.tb == MG_T;
   int best = -1;
-  int64_t best_area = -1;
+  int64_t bk0 = 0, bk1 = 0, bk2 = 0, bk3 = 0;
   for (int i = 0; i < n; ++i) {
-    if (!e[i].a_vec || !e[i].b_vec) continue;
-    const int64_t t = tiles_for(M, N, e[i].bm, e[i].bn);
+    if (!e[i].a_vec || !e[i].b_vec || e[i].fn[c][akc][bkc] == nullptr) continue;
+    const int64_t t = tiles_for(p.M, p.N, e[i].bm, e[i].bn);
     const int64_t area = (int64_t)e[i].bm * e[i].bn;
-    if (t >= 256 && area > best_area) {
+    const int64_t k0 = t >= 256, k1 = t >= 256 ? area : t, k2 = t >= 256 ? e[i].kind : area,
+                  k3 = t >= 256 ? 0 : e[i].kind;
+    if (best < 0 || k0 > bk0 || (k0 == bk0 && (k1 > bk1 || (k1 == bk1 && (k2 > bk2 ||
+        (k2 == bk2 && k3 > bk3)))))) {
       best = i;
-      best_area = area;
-    }
-  }
-  if (best >= 0) return best;
-  int64_t most = -1;
-  for (int i = 0; i < n; ++i) {
-    if (!e[i].a_vec || !e[i].b_vec) continue;
-    const int64_t t = tiles_for(M, N, e[i].bm, e[i].bn);
-    if (t > most || (t == most && best >= 0 &&
-                     (int64_t)e[i].bm * e[i].bn > (int64_t)e[best].bm * e[best].bn)) {
-      most = t;
-      best = i;
+      bk0 = k0; bk1 = k1; bk2 = k2; bk3 = k3;
     }
   }
   return best;
@@ -190,7 +184,12 @@ Plan plan(const Problem &p) {
   pl.b_vec = vec_ok(p.B, p.ldb, b_kc ? p.K : p.N, es);
   if (pl.a_vec && pl.b_vec) {
     int c = table_config(p);
-    pl.config = c >= 0 ? c : heuristic_config(p.in_type, p.M, p.N);
+    if (c >= 0) {
+      int n = 0;
+      const KernelEntry *e = entries(p.in_type, &n);
+      if (e[c].fn[p.c_type == MG_F32 ? 1 : 0][a_kc ? 1 : 0][b_kc ? 1 : 0] == nullptr) c = -1;
+    }
+    pl.config = c >= 0 ? c : heuristic_config(p);
   } else {
     pl.config = elem_config(p.in_type, pl.a_vec, pl.b_vec);
   }
@@ -234,6 +233,8 @@ static mg_status run(const Problem &p, int forced, void *stream_v) {
     if (cfg < 0) return MG_EUNSUPPORTED;
     const KernelEntry &k = e[cfg];
     if ((k.a_vec && !pl.a_vec) || (k.b_vec && !pl.b_vec)) return MG_EUNSUPPORTED;
+    const int ci = (p.c_type == MG_F32) ? 1 : 0, ak = p.ta == MG_N ? 1 : 0, bk = p.tb == MG_T ? 1 : 0;
+    if (k.fn[ci][ak][bk] == nullptr) return MG_EUNSUPPORTED;
     gp.tiles_m = (int)((p.M + k.bm - 1) / k.bm);
     gp.tiles_n = (int)((p.N + k.bn - 1) / k.bn);
     gp.group_m = 8;

@@ -67,21 +67,23 @@ def test_mfma_layout_probe_identity():
 
 @pytest.mark.parametrize("in_dtype", ["f32", "f16", "bf16"])
 def test_every_config_every_layout_integer_bit_exact(in_dtype):
-    """Forced configurations: vector-load variants on 16-byte-loadable shapes
-    (still ragged against every tile), element-load variants on odd shapes."""
+    """Forced configurations.  Every configuration runs on a shape whose
+    operands are 16-byte loadable but ragged against every tile; the
+    all-element-load configuration also runs on an odd shape."""
     import dense_gemm_12_amd as mg
     n = mg.num_configs(in_dtype)
-    shapes = {True: (296, 272, 200), False: (300, 270, 201)}
     for (ta, tb) in LAYOUTS:
         for c_dtype in C_TYPES[in_dtype]:
-            for vec, (M, N, K) in shapes.items():
+            for (M, N, K), only_elem_ab in (((296, 272, 200), False), ((300, 270, 201), True)):
                 A, B, C = make(M, N, K, ta, tb, in_dtype, c_dtype, "int2", 11)
                 ref = oracle_full(A, B, C, alpha=1.5, beta=0.5, ta=ta, tb=tb, in_dtype=in_dtype,
                                   c_dtype=c_dtype)
                 for cfg in range(n):
                     name = mg.config_name(in_dtype, cfg)
-                    if name.startswith("mfma") != vec:
+                    if only_elem_ab and not name.startswith("elemAB"):
                         continue
+                    if name.startswith("dma") and (ta or not tb):
+                        continue  # direct-to-LDS kernels take k-contiguous A and B only
                     what = f"{name} ta={ta} tb={tb} c={c_dtype} {M}x{N}x{K}"
                     log("case " + what)
                     got = run_gpu(A, B, C, alpha=1.5, beta=0.5, ta=ta, tb=tb, c_dtype=c_dtype,
