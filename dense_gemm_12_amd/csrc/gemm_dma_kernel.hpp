@@ -1,27 +1,29 @@
-// 16-bit-input GEMM for operands whose k dimension is contiguous in memory
-// (A stored M x K, B stored N x K: the "TN" layout of "HGEMM SMEM Swizzle
-// 代码学习" and "Warp Specialization HGEMM" section 6), built around gfx950's
-// global->LDS DMA:
+// 16-bit-input GEMM built around gfx950's global->LDS DMA, for every storage
+// layout of A and B:
 //
 //   * buffer_load_dwordx4 ... lds moves each 16-byte chunk from HBM straight
 //     into LDS without passing through VGPRs, so no staging registers and no
 //     ds_write instructions are spent on the copy;
 //   * one DMA instruction writes 64 lanes x 16 bytes = 1 KiB of LDS at
 //     consecutive addresses, so rows cannot be padded; bank conflicts on the
-//     fragment reads are avoided instead by an XOR swizzle of the 16-byte
-//     chunk index within each row (the idea "HGEMM SMEM Swizzle 代码学习"
-//     applies to ldmatrix, re-derived here for CDNA4's LDS and wave64: the 16
-//     rows one quarter-wave reads land in 16 distinct 16-byte bank groups of
-//     a 256-byte window, and any 8 aligned rows in 8 distinct groups of a
-//     128-byte window).  The DMA side applies the same permutation when it
+//     fragment reads are avoided instead by XOR-permuting the 16-byte chunks
+//     within each LDS row (the idea "HGEMM SMEM Swizzle 代码学习" applies to
+//     ldmatrix; the permutations here were chosen by measuring gfx950's LDS
+//     conflict counters).  The DMA side applies the same permutation when it
 //     picks which global chunk each lane fetches;
-//   * STAGES slices ring through LDS: the loads for slice k+STAGES-1 are
-//     issued right after the barrier that releases its buffer, so HBM latency
-//     is covered by STAGES-1 slices of MFMA work ("SGEMM CUDA代码学习" step 5's
-//     multistage pipeline, restated for vmcnt-counted DMA);
-//   * each wave reads the fragments of the next k-step while the MFMAs of the
-//     current one run (the two-level buffering the worklog's closing notes
-//     describe).
+//   * an operand whose k dimension is contiguous in memory (A stored M x K, B
+//     stored N x K: the "TN" layout of "HGEMM SMEM Swizzle 代码学习" and of "Warp
+//     Specialization HGEMM" section 6) is staged as [row][k] and read with one
+//     ds_read_b128 per 16x32 fragment; a k-major operand (A stored K x M, B
+//     stored K x N as in the plain row-major problem of "SGEMM CUDA代码学习") is
+//     staged untouched as [k][row] and read with two ds_read_b64_tr_b16, the
+//     gfx950 LDS read that transposes 16-bit elements across each group of 16
+//     lanes, so no layout ever needs a transpose pass or register shuffles;
+//   * STAGES slices ring through LDS and each wave reads the fragments of the
+//     next k-step while the MFMAs of the current one run ("SGEMM CUDA代码学习"
+//     steps 4-5 and the worklog's closing notes on two-level buffering,
+//     restated for vmcnt-counted DMA); the issue order of MFMAs, LDS reads
+//     and DMA is fixed with scheduling fences.
 // Tails: rows past M/N and k past K are fetched with an out-of-range buffer
 // offset, which makes the DMA write zeros; slices beyond the last one are
 // issued the same way so the vmcnt bookkeeping never changes.
@@ -33,12 +35,7 @@
 namespace mg {
 
 typedef __attribute__((address_space(3))) void lds_void;
-
-template <int CPR>
-__device__ __forceinline__ int chunk_swizzle(int r) {
-  if constexpr (CPR == 8) return (r & 7) ^ ((r >> 3) & 1);
-  else return ((r >> 1) & 3) ^ ((r >> 3) & 1);
-}
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -47,42 +44,126 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xf) | (0x7 << 4) | (0xf << 8) | ((N >> 4) << 14));
 }
 
-template <typename TI, typename TO, int BM_, int BN_, int BK_, int STAGES_, int WAVES_M, int WAVES_N>
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
+// Workgroup barrier for LDS hand-offs whose completion the caller has
+// already established with explicit vmcnt/lgkmcnt waits.  Unlike
+// __syncthreads() it carries no memory fence, so DMA issued for later slices
+// stays in flight across it; the empty asm statements keep the compiler from
+// moving LDS accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One operand slice (R rows of the operand x BK values of k) in LDS.
+//
+// KC = true, k contiguous in memory: LDS rows are operand rows of BK*2
+// bytes; 16-byte chunk c of row r sits at slot c ^ swz(r), swz(r) = r mod 8
+// (128-byte rows) or (r / 2) mod 4 (64-byte rows).  Lane l's fragment for
+// 16-row block b, k-step ks is row 16b + l%16, chunk 4ks + l/16: one
+// ds_read_b128.
+//
+// KC = false, operand rows contiguous in memory: LDS rows are the BK k
+// values, each R*2 bytes; chunk c of k-row k sits at slot c ^ swz(k),
+// swz(k) = 2 * ((k mod 4) | ((k / 8) mod 2) * 4), an even value so the two
+// 16-byte chunks of each 32-byte span stay adjacent.  ds_read_b64_tr_b16
+// returns to lane j of a 16-lane group element j%4 of the 8-byte reads of
+// lanes j/4, j/4+4, j/4+8, j/4+12 of the group; so lane i of group g reads
+// k-row 8g + 4h + i/4 at columns 16b + 4(i%4) .. +3 and receives, for its own
+// column 16b + j, the four k values 8g + 4h .. +3.  Two reads (h = 0, 1)
+// give the 8 k values of the MFMA operand.
+template <int R, int BK, bool KC, int NW>
+struct DmaOperand {
+  static constexpr int BYTES = R * BK * 2;
+  static constexpr int INST = BYTES / 1024 / NW;  // DMA instructions per wave per slice
+  static constexpr int ROWB = KC ? BK * 2 : R * 2;
+  static constexpr int CPR = ROWB / 16;
+  static constexpr int RPB = 1024 / ROWB;         // LDS rows per 1 KiB DMA block
+  static constexpr int READS = KC ? 1 : 2;        // LDS reads per 16-row fragment
+  static_assert(BYTES % (1024 * NW) == 0, "whole DMA blocks per wave");
+  static_assert(KC ? (CPR == 4 || CPR == 8) : (CPR >= 16), "supported LDS row widths");
+
+  static __device__ __forceinline__ int swz(int row) {
+    if constexpr (KC) return CPR == 8 ? (row & 7) : ((row >> 1) & 3);
+    else return 2 * ((row & 3) | (((row >> 3) & 1) << 2));
+  }
+
+  // DMA instruction u of this wave for one slice.  rs: buffer at the stored
+  // element (r0, k0) (KC) or (k0, r0) (k-major); ldb: row pitch in bytes;
+  // rv / kv: operand rows and k values still inside the matrix.
+  static __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t rs, uint32_t ldb, int rv, int kv,
+                                             char *dst, int wave, int lane, int u) {
+    const int blk = wave * INST + u;
+    const int row = blk * RPB + lane / CPR;
+    const int c = (lane % CPR) ^ swz(row);
+    const bool ok = KC ? (row < rv && c * 8 < kv) : (row < kv && c * 8 < rv);
+    const uint32_t off = ok ? row * ldb + c * 16 : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + blk * 1024), 16, off, 0, 0, 0);
+  }
+
+  // Per-lane fragment addressing.  rowblk0: first 16-row block of the wave
+  // within the slice; NB: blocks per wave; KSTEPS: k-steps per slice.
+  template <int NB, int KSTEPS>
+  struct Frag {
+    int base;
+    int xo[KC ? KSTEPS : NB];
+
+    __device__ __forceinline__ void init(int lane, int rowblk0) {
+      const int j = lane & 15, g = lane >> 4;
+      if constexpr (KC) {
+        base = (rowblk0 * 16 + j) * ROWB;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) xo[ks] = ((ks * 4 + g) ^ swz(j)) * 16;
+      } else {
+        const int gk = 2 * ((j >> 2) | ((g & 1) << 2));  // swz of the lane's k-row
+        base = (8 * g + (j >> 2)) * ROWB + 8 * (j & 1);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) xo[b] = ((((rowblk0 + b) * 2) ^ gk) + ((j >> 1) & 1)) * 16;
+      }
+    }
+
+    // Read number h (0 .. READS-1) of fragment (block b, k-step ks) into f.
+    __device__ __forceinline__ void read(const char *st, int b, int ks, int h, u32x4 &f) const {
+      if constexpr (KC) {
+        f = *reinterpret_cast<const u32x4 *>(st + base + b * 16 * ROWB + xo[ks]);
+      } else {
+        const char *pa = st + base + (ks * 32 + 4 * h) * ROWB + xo[b];
+        const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4 *)((__attribute__((address_space(3))) char *)pa));
+        const u32x2 w = __builtin_bit_cast(u32x2, v);
+        if (h == 0) {
+          f.x = w.x;
+          f.y = w.y;
+        } else {
+          f.z = w.x;
+          f.w = w.y;
+        }
+      }
+    }
+  };
+};
+
+template <typename TI, typename TO, int BM_, int BN_, int BK_, int STAGES_, int WAVES_M, int WAVES_N,
+          bool A_KC, bool B_KC>
 struct DmaTile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
   static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
-  static constexpr int ROWB = BK * 2;              // LDS row bytes (16-bit elements)
-  static constexpr int CPR = ROWB / 16;            // 16-byte chunks per row
-  static constexpr int RPB = 1024 / ROWB;          // rows per 1 KiB DMA block
-  static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
+  using OA = DmaOperand<BM, BK, A_KC, NW>;
+  using OB = DmaOperand<BN, BK, B_KC, NW>;
+  static constexpr int A_BYTES = OA::BYTES, B_BYTES = OB::BYTES;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  static constexpr int A_INST = A_BYTES / 1024 / NW, B_INST = B_BYTES / 1024 / NW;
+  static constexpr int A_INST = OA::INST, B_INST = OB::INST;
   static constexpr int LOADS_PER_SLICE = A_INST + B_INST;
   static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   static constexpr int MI = WTM / 16, NJ = WTN / 16;
   static constexpr int KSTEPS = BK / 32;           // 16x16x32 MFMA k-steps per slice
-  static_assert(CPR == 4 || CPR == 8, "BK must be 32 or 64");
-  static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "whole DMA blocks");
+  static constexpr int RD_B = NJ * OB::READS, RD_A = MI * OA::READS;
+  static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
   static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS budget");
   static_assert(LOADS_PER_SLICE * (STAGES - 1) < 64, "vmcnt range");
-
-  // Issue the DMA for one operand slice.  base: byte address of stored
-  // element (r0, k0); ldb: row pitch in bytes; rv/kv: rows and k left.
-  template <int INST>
-  static __device__ __forceinline__ void dma(const char *base, uint32_t ldb, int rv, int kv,
-                                             char *lds, int wave, int lane) {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
-    const int slot = lane % CPR;
-#pragma unroll
-    for (int i = 0; i < INST; ++i) {
-      const int blk = wave * INST + i;
-      const int row = blk * RPB + lane / CPR;
-      const int c = slot ^ chunk_swizzle<CPR>(row);
-      const bool ok = row < rv && c * 8 < kv;
-      const uint32_t off = ok ? row * ldb + c * 16 : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds + blk * 1024), 16, off, 0, 0, 0);
-    }
-  }
 
   static __device__ __forceinline__ void run(const GemmParams &p) {
     __shared__ __attribute__((aligned(1024))) char lds[STAGES * STAGE_BYTES];
@@ -94,17 +175,27 @@ struct DmaTile {
     tile_coords(remap_xcd(blockIdx.x, p.tiles_m * p.tiles_n), p.tiles_m, p.tiles_n, p.group_m, tm,
                 tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const char *Ab = static_cast<const char *>(p.A) + (int64_t)m0 * p.lda * 2;
-    const char *Bb = static_cast<const char *>(p.B) + (int64_t)n0 * p.ldb * 2;
+    // Slice origins advance by BK along k: BK elements for a k-contiguous
+    // operand, BK rows for a k-major one.
+    const char *Ab = static_cast<const char *>(p.A) + (A_KC ? (int64_t)m0 * p.lda : m0) * 2;
+    const char *Bb = static_cast<const char *>(p.B) + (B_KC ? (int64_t)n0 * p.ldb : n0) * 2;
+    const int64_t a_step = (A_KC ? BK : (int64_t)BK * p.lda) * 2;
+    const int64_t b_step = (B_KC ? BK : (int64_t)BK * p.ldb) * 2;
     const uint32_t lda_b = (uint32_t)(p.lda * 2), ldb_b = (uint32_t)(p.ldb * 2);
     const int rva = p.M - m0, rvb = p.N - n0;
     const int nk = (p.K + BK - 1) / BK;
 
-    auto issue = [&](int kt) {
+    auto dma_op = [&](int kt, int u) {  // DMA instruction u (A first, then B) of slice kt
       char *st = lds + (kt % STAGES) * STAGE_BYTES;
       const int kv = p.K - kt * BK;
-      dma<A_INST>(Ab + (int64_t)kt * BK * 2, lda_b, rva, kv, st, wave, lane);
-      dma<B_INST>(Bb + (int64_t)kt * BK * 2, ldb_b, rvb, kv, st + A_BYTES, wave, lane);
+      if (u < A_INST)
+        OA::dma(make_rsrc(Ab + kt * a_step), lda_b, rva, kv, st, wave, lane, u);
+      else
+        OB::dma(make_rsrc(Bb + kt * b_step), ldb_b, rvb, kv, st + A_BYTES, wave, lane, u - A_INST);
+    };
+    auto issue = [&](int kt) {
+#pragma unroll
+      for (int u = 0; u < LOADS_PER_SLICE; ++u) dma_op(kt, u);
     };
 
     f32x4 acc[MI][NJ];
@@ -113,50 +204,135 @@ struct DmaTile {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Per-lane fragment offsets: row (lane % 16) of each 16-row block, chunk
-    // (ks*4 + lane/16) un-swizzled by the row's pattern (which only depends
-    // on the row modulo 16).
-    const int lrow = lane & 15;
-    const int sw = chunk_swizzle<CPR>(lrow);
-    int coff[KSTEPS];
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) coff[ks] = (((ks * 4 + (lane >> 4)) ^ sw) * 16);
-    const int a_row0 = (wm * WTM + lrow) * ROWB;
-    const int b_row0 = A_BYTES + (wn * WTN + lrow) * ROWB;
+    typename OA::template Frag<MI, KSTEPS> fra;
+    typename OB::template Frag<NJ, KSTEPS> frb;
+    fra.init(lane, wm * MI);
+    frb.init(lane, wn * NJ);
 
+    // Memory op t of a fragment set: B-side reads first, then A-side.
+    auto read_op = [&](const char *st, int ks, int t, u32x4 (&fa)[MI], u32x4 (&fb)[NJ]) {
+      if (t < RD_B) frb.read(st + A_BYTES, t / OB::READS, ks, t % OB::READS, fb[t / OB::READS]);
+      else fra.read(st, (t - RD_B) / OA::READS, ks, (t - RD_B) % OA::READS, fa[(t - RD_B) / OA::READS]);
+    };
+    auto read_frags = [&](const char *st, int ks, u32x4 (&fa)[MI], u32x4 (&fb)[NJ]) {
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) issue(s);
-
-    for (int kt = 0; kt < nk; ++kt) {
-      wait_vmcnt<LOADS_PER_SLICE * (STAGES - 2)>();
-      __syncthreads();
-      issue(kt + STAGES - 1);
-      const char *st = lds + (kt % STAGES) * STAGE_BYTES;
-      u32x4 fa[2][MI], fb[2][NJ];
+      for (int t = 0; t < RD_A + RD_B; ++t) read_op(st, ks, t, fa, fb);
+    };
+    auto mfmas = [&](const u32x4 (&fa)[MI], const u32x4 (&fb)[NJ]) {
 #pragma unroll
       for (int i = 0; i < MI; ++i)
-        fa[0][i] = *reinterpret_cast<const u32x4 *>(st + a_row0 + i * 16 * ROWB + coff[0]);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        fb[0][j] = *reinterpret_cast<const u32x4 *>(st + b_row0 + j * 16 * ROWB + coff[0]);
+        for (int j = 0; j < NJ; ++j) Mfma<TI>::step(acc[i][j], fb[j], fa[i]);
+    };
+
+    if constexpr (STAGES == 2 && KSTEPS == 2) {
+      // Mid-slice barrier schedule.  Per slice kt (buffer S = kt % 2):
+      //   phase A: MFMAs of k-step 0, each followed by at most one LDS read
+      //            of the k-step 1 fragments of slice kt;
+      //   wait for slice kt+1's DMA and for this wave's reads; barrier: every
+      //   wave now holds all of slice kt's fragments, so buffer S is free;
+      //   phase C: MFMAs of k-step 1, each followed by at most one DMA issue
+      //            for slice kt+2 (into S) or one LDS read of slice kt+1's
+      //            k-step 0 fragments.
+      // (With more memory ops than MFMAs, each MFMA is followed by up to
+      // ceil(ops / MFMAs) of them.)  The MFMAs never wait on an LDS read; the
+      // barrier is the only point where the matrix pipe can drain.
+      constexpr int SLOTS = MI * NJ;
+      constexpr int PA = (RD_A + RD_B + SLOTS - 1) / SLOTS;                    // ops per MFMA, phase A
+      constexpr int PC = (LOADS_PER_SLICE + RD_A + RD_B + SLOTS - 1) / SLOTS;  // ops per MFMA, phase C
+      u32x4 fa0[MI], fb0[NJ], fa1[MI], fb1[NJ];
+      issue(0);
+      issue(1);
+      wait_vmcnt<LOADS_PER_SLICE>();
+      __syncthreads();
+      read_frags(lds, 0, fa0, fb0);
+      for (int kt = 0; kt < nk; ++kt) {
+        const char *st = lds + (kt & 1) * STAGE_BYTES;
+        const char *nx = lds + ((kt + 1) & 1) * STAGE_BYTES;
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int cur = ks & 1, nxt = cur ^ 1;
-        if (ks + 1 < KSTEPS) {
+        for (int t = 0; t < MI * NJ; ++t) {  // phase A
+          Mfma<TI>::step(acc[t / NJ][t % NJ], fb0[t % NJ], fa0[t / NJ]);
 #pragma unroll
-          for (int i = 0; i < MI; ++i)
-            fa[nxt][i] = *reinterpret_cast<const u32x4 *>(st + a_row0 + i * 16 * ROWB + coff[ks + 1]);
-#pragma unroll
-          for (int j = 0; j < NJ; ++j)
-            fb[nxt][j] = *reinterpret_cast<const u32x4 *>(st + b_row0 + j * 16 * ROWB + coff[ks + 1]);
+          for (int o = t * PA; o < (t + 1) * PA; ++o)
+            if (o < RD_A + RD_B) read_op(st, 1, o, fa1, fb1);
+          __builtin_amdgcn_sched_barrier(0);
         }
+        wait_vmcnt<0>();
+        wait_lgkm0();  // this wave's reads of S are done
+        __syncthreads();
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
+        for (int t = 0; t < MI * NJ; ++t) {  // phase C
+          Mfma<TI>::step(acc[t / NJ][t % NJ], fb1[t % NJ], fa1[t / NJ]);
 #pragma unroll
-          for (int j = 0; j < NJ; ++j) Mfma<TI>::step(acc[i][j], fb[cur][j], fa[cur][i]);
+          for (int o = t * PC; o < (t + 1) * PC; ++o) {
+            if (o < LOADS_PER_SLICE) dma_op(kt + 2, o);
+            else if (o < LOADS_PER_SLICE + RD_A + RD_B) read_op(nx, 0, o - LOADS_PER_SLICE, fa0, fb0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    } else if constexpr (STAGES >= 3 && KSTEPS == 1) {
+      // Ring schedule for one-k-step slices.  During slice kt each wave runs
+      // its MFMAs on slice kt's fragments (in registers), interleaved with
+      // the LDS reads of slice kt+1's fragments and the DMA of slice
+      // kt+STAGES into buffer kt % STAGES (free: slice kt's fragments were
+      // read by every wave before the previous barrier).  The barrier at the
+      // end of slice kt waits only for slice kt+2, so STAGES-1 slices of DMA
+      // stay in flight.
+      constexpr int SLOTS = MI * NJ;
+      constexpr int PO = (LOADS_PER_SLICE + RD_A + RD_B + SLOTS - 1) / SLOTS;  // ops per MFMA
+      u32x4 fa[2][MI], fb[2][NJ];
+#pragma unroll
+      for (int s = 0; s < STAGES; ++s) issue(s);
+      wait_vmcnt<LOADS_PER_SLICE * (STAGES - 2)>();
+      lds_barrier();
+      read_frags(lds, 0, fa[0], fb[0]);
+      // Slice 0's buffer is refilled during slice 0: every wave must have
+      // its slice-0 fragments before anyone issues that DMA.
+      wait_lgkm0();
+      lds_barrier();
+      for (int kt = 0; kt < nk; kt += 2) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {  // two slices per trip keep fragment buffers static
+          const int k = kt + h;
+          const char *nx = lds + ((k + 1) % STAGES) * STAGE_BYTES;
+#pragma unroll
+          for (int t = 0; t < MI * NJ; ++t) {
+            Mfma<TI>::step(acc[t / NJ][t % NJ], fb[h][t % NJ], fa[h][t / NJ]);
+#pragma unroll
+            for (int o = t * PO; o < (t + 1) * PO; ++o) {
+              if (o < RD_A + RD_B) read_op(nx, 0, o, fa[h ^ 1], fb[h ^ 1]);
+              else if (o < RD_A + RD_B + LOADS_PER_SLICE) dma_op(k + STAGES, o - RD_A - RD_B);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (k + 1 >= nk) break;
+          wait_vmcnt<LOADS_PER_SLICE * (STAGES - 2)>();  // slice k+2 has landed
+          wait_lgkm0();                                   // slice k+1's reads are done
+          lds_barrier();
+        }
+      }
+    } else {
+      // Plain multistage loop: one barrier per slice, next k-step's
+      // fragments read while the current one's MFMAs run.
+#pragma unroll
+      for (int s = 0; s < STAGES - 1; ++s) issue(s);
+      for (int kt = 0; kt < nk; ++kt) {
+        wait_vmcnt<LOADS_PER_SLICE * (STAGES - 2)>();
+        __syncthreads();
+        issue(kt + STAGES - 1);
+        const char *st = lds + (kt % STAGES) * STAGE_BYTES;
+        u32x4 fa[2][MI], fb[2][NJ];
+        read_frags(st, 0, fa[0], fb[0]);
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          if (ks + 1 < KSTEPS) read_frags(st, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+          mfmas(fa[ks & 1], fb[ks & 1]);
+        }
       }
     }
 
+    wait_vmcnt<0>();  // the trailing (all out-of-range) DMA has landed before the LDS is released
     GemmEpilogue<TO, MI, NJ>::store(p, acc, m0 + wm * WTM, n0 + wn * WTN, lane);
   }
 };

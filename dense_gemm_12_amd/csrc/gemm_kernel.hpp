@@ -9,8 +9,11 @@
 //     into LDS, always as [row][k] with k contiguous, through 16-byte buffer
 //     loads; a k-major operand (A stored K x M, or B stored K x N) is
 //     transposed in registers on the way, so the MFMA feed never strides;
-//   * LDS rows are padded by 16 bytes, which spreads the 16 rows a quarter
-//     wave reads with one ds_read_b128 over distinct 16-byte bank groups;
+//   * LDS rows are 128 bytes with the 16-byte chunk index XORed with
+//     (row mod 8): measured on gfx950, this keeps both the ds_write_b128 of
+//     the staging (8 lanes per 128-byte row) and the ds_read_b128 fragment
+//     reads (16 rows, one chunk per quarter-wave) free of bank conflicts,
+//     where a 16-byte row pad still conflicts 2-way on the reads;
 //   * two LDS buffers alternate: while the waves run MFMAs on slice k the
 //     global loads for slice k+1 are in flight in registers, and one barrier
 //     per slice separates the buffer swap ("SGEMM CUDA代码学习" step 4; the
@@ -39,7 +42,8 @@ struct SliceLoader {
   static constexpr int V = 16 / ES;            // elements per 16-byte chunk
   static constexpr int KCH = BK / V;           // chunks per LDS row
   static constexpr int NCH = BR * KCH;         // chunks per slice
-  static constexpr int PITCH = BK * ES + 16;   // LDS row pitch (bytes)
+  static constexpr int PITCH = BK * ES;        // LDS row pitch (bytes), unpadded
+  static_assert(PITCH == 128, "rows are 8 chunks: the XOR swizzle below assumes it");
   static constexpr int NBLK = KC ? NCH : NCH / V;  // work items (chunk or V x V block)
   static constexpr int ITERS = (NBLK + NT - 1) / NT;
   static constexpr int NREG = KC ? ITERS : ITERS * V;
@@ -90,12 +94,14 @@ struct SliceLoader {
       if (NBLK % NT != 0 && w >= NBLK) break;
       if constexpr (KC) {
         const int row = w / KCH, kc = w % KCH;
-        *reinterpret_cast<u32x4 *>(lds + row * PITCH + kc * 16) = r[it];
+        *reinterpret_cast<u32x4 *>(lds + row * PITCH + ((kc ^ (row & 7)) * 16)) = r[it];
       } else {
         const int kb = w % KCH, rb = w / KCH;
 #pragma unroll
-        for (int i = 0; i < V; ++i)
-          *reinterpret_cast<u32x4 *>(lds + (rb * V + i) * PITCH + kb * 16) = r[it * V + i];
+        for (int i = 0; i < V; ++i) {
+          const int row = rb * V + i;
+          *reinterpret_cast<u32x4 *>(lds + row * PITCH + ((kb ^ (row & 7)) * 16)) = r[it * V + i];
+        }
       }
     }
   }
@@ -177,30 +183,29 @@ struct GemmTile {
   static constexpr int ES = sizeof(TI);
   static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;  // wave sub-tile
   static constexpr int MI = WTM / 16, NJ = WTN / 16;            // 16x16 blocks per wave
-  static constexpr int KSUB_BYTES = 64;                         // 4 lane groups x 16 bytes
-  static constexpr int KSTEPS = BK * ES / KSUB_BYTES;
+  static constexpr int KSTEPS = BK * ES / 64;                   // 4 lane groups x 16 bytes
   using LA = SliceLoader<ES, BM, BK, A_KC, A_VEC, NT>;
   using LB = SliceLoader<ES, BN, BK, B_KC, B_VEC, NT>;
   static constexpr int PITCH = LA::PITCH;
   static constexpr int STAGE_BYTES = (BM + BN) * PITCH;
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be whole MFMA blocks");
-  static_assert((BK * ES) % KSUB_BYTES == 0, "BK must be whole k-steps");
+  static_assert((BK * ES) % 64 == 0, "BK must be whole k-steps");
   static_assert(2 * STAGE_BYTES <= 160 * 1024, "LDS budget");
 
   static __device__ __forceinline__ void compute(const char *sa, const char *sb, f32x4 (&acc)[MI][NJ],
                                                  int lane, int wm, int wn) {
-    const int lrow = lane & 15, lk = (lane >> 4) * 16;
+    const int lrow = lane & 15;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
+      // chunk (ks*4 + lane/16) of rows whose index mod 8 is lrow mod 8
+      const int col = (((ks * 4 + (lane >> 4)) ^ (lrow & 7)) * 16);
       u32x4 a[MI], b[NJ];
 #pragma unroll
       for (int i = 0; i < MI; ++i)
-        a[i] = *reinterpret_cast<const u32x4 *>(sa + (wm * WTM + i * 16 + lrow) * PITCH +
-                                                ks * KSUB_BYTES + lk);
+        a[i] = *reinterpret_cast<const u32x4 *>(sa + (wm * WTM + i * 16 + lrow) * PITCH + col);
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
-        b[j] = *reinterpret_cast<const u32x4 *>(sb + (wn * WTN + j * 16 + lrow) * PITCH +
-                                                ks * KSUB_BYTES + lk);
+        b[j] = *reinterpret_cast<const u32x4 *>(sb + (wn * WTN + j * 16 + lrow) * PITCH + col);
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll

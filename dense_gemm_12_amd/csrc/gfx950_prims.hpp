@@ -49,18 +49,21 @@ __device__ __forceinline__ uint16_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t
 template <typename T> struct Mfma;
 
 template <> struct Mfma<_Float16> {
+  static constexpr int kInsts = 1;
   static __device__ __forceinline__ void step(f32x4 &acc, const u32x4 &a, const u32x4 &b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                  __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
   }
 };
 template <> struct Mfma<__bf16> {
+  static constexpr int kInsts = 1;
   static __device__ __forceinline__ void step(f32x4 &acc, const u32x4 &a, const u32x4 &b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                   __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
   }
 };
 template <> struct Mfma<float> {
+  static constexpr int kInsts = 4;
   static __device__ __forceinline__ void step(f32x4 &acc, const u32x4 &a, const u32x4 &b) {
     const f32x4 fa = __builtin_bit_cast(f32x4, a), fb = __builtin_bit_cast(f32x4, b);
 #pragma unroll

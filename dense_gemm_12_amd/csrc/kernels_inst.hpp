@@ -50,8 +50,19 @@ hipError_t launch_dma_tile(const GemmParams &p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Direct-to-LDS configurations exist for the k-contiguous layout of both
-// operands only (A stored M x K, B stored N x K).
+template <typename TI, typename TO, int BM, int BN, int BK, int ST, int WM, int WN>
+struct DmaLayoutSet {
+  template <bool AKC, bool BKC>
+  using T = DmaTile<TI, TO, BM, BN, BK, ST, WM, WN, AKC, BKC>;
+  static void fill(LaunchFn (&f)[2][2]) {
+    f[0][0] = &launch_dma_tile<T<false, false>>;
+    f[0][1] = &launch_dma_tile<T<false, true>>;
+    f[1][0] = &launch_dma_tile<T<true, false>>;
+    f[1][1] = &launch_dma_tile<T<true, true>>;
+  }
+};
+
+// Direct-to-LDS configurations (16-bit inputs, 16-byte-loadable operands).
 template <typename TI, typename TO16, int BM, int BN, int BK, int ST, int WM, int WN>
 KernelEntry make_dma_entry(const char *name) {
   KernelEntry e{};
@@ -62,8 +73,8 @@ KernelEntry make_dma_entry(const char *name) {
   e.a_vec = true;
   e.b_vec = true;
   e.kind = 1;
-  e.fn[1][1][1] = &launch_dma_tile<DmaTile<TI, float, BM, BN, BK, ST, WM, WN>>;
-  e.fn[0][1][1] = &launch_dma_tile<DmaTile<TI, TO16, BM, BN, BK, ST, WM, WN>>;
+  DmaLayoutSet<TI, float, BM, BN, BK, ST, WM, WN>::fill(e.fn[1]);
+  DmaLayoutSet<TI, TO16, BM, BN, BK, ST, WM, WN>::fill(e.fn[0]);
   return e;
 }
 

@@ -1,0 +1,224 @@
+"""rocprofv3 harness: hardware counters of the GEMM kernels against MI355X's peaks.
+
+Two modes:
+
+``python -m dense_gemm_12_amd.rocprof_harness run --workload fp16_tn_4096 --out DIR``
+    Runs one rocprofv3 pass per counter group (each group stays within the
+    per-block limits of one pass), each over ``target`` below, then parses
+    the CSV output and writes ``DIR/summary.json`` and ``DIR/summary.md``:
+    MFMA utilisation, VALU busy, LDS bank-conflict rate, effective shader
+    clock, HBM-side traffic (FETCH_SIZE / WRITE_SIZE calibrated against a
+    plain copy of known size) and achieved TFLOPS / GB/s against the peaks.
+
+``python -m dense_gemm_12_amd.rocprof_harness target --workload NAME [--iters N] [--config C]``
+    The program each pass profiles: uploads the workload's seeded inputs and
+    runs the library's GEMM ``iters`` times; ``--workload copy`` instead runs a
+    1 GiB device-to-device copy (the calibration kernel).
+
+The driver never touches the GPU itself; each pass is a fresh process started
+directly by rocprofv3.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CUS, SIMDS = 256, 1024
+PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6}
+HBM_GBPS = 8000.0
+COPY_BYTES = 1 << 30
+
+# One rocprofv3 pass per group: <= 8 SQ, <= 4 TCC (FETCH_SIZE uses 3,
+# WRITE_SIZE 2), <= 2 GRBM counters.
+PASSES = {
+    "fetch": ["FETCH_SIZE", "GRBM_GUI_ACTIVE"],
+    "write": ["WRITE_SIZE", "GRBM_GUI_ACTIVE"],
+    "sq": ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_LDS_BANK_CONFLICT",
+           "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_BUSY_CU_CYCLES",
+           "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE"],
+}
+
+
+def _target(args):
+    sys.path.insert(0, ROOT)
+    import torch
+    import gemm_inputs as gi
+    import dense_gemm_12_amd as mg
+    dev = torch.device("cuda:0")
+    if args.workload == "copy":
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.iters):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copy x{args.iters} done", flush=True)
+        return
+    w = gi.WORKLOADS[args.workload]
+    A, B, C = gi.workload_inputs(args.workload)
+    Ad, Bd = A.to(dev), B.to(dev)
+    Cd = C.to(dev) if C is not None else torch.zeros((w["M"], w["N"]), dtype=gi.DTYPES[w["c_dtype"]],
+                                                     device=dev)
+    cfg = -1 if args.config is None else mg.config_id(w["in_dtype"], args.config)
+    for _ in range(args.iters):
+        mg.gemm(Ad, Bd, Cd, alpha=w["alpha"], beta=w["beta"], trans_a=w["ta"], trans_b=w["tb"],
+                config=cfg)
+    torch.cuda.synchronize()
+    print(f"{args.workload} x{args.iters} done", flush=True)
+
+
+def _read_counters(pass_dir):
+    """{kernel name: {counter: [per-dispatch values]}} plus durations (ns)."""
+    files = glob.glob(os.path.join(pass_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise RuntimeError(f"no counter_collection.csv under {pass_dir}")
+    per = {}
+    for f in files:
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                k = row["Kernel_Name"]
+                d = per.setdefault(k, {"dispatch": {}})
+                key = row.get("Dispatch_Id") or row.get("Correlation_Id")
+                disp = d["dispatch"].setdefault(key, {})
+                disp[row["Counter_Name"]] = disp.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+                for tk in ("Start_Timestamp", "End_Timestamp"):
+                    if row.get(tk):
+                        disp[tk] = float(row[tk])
+    return per
+
+
+def _avg(per_kernel, counter):
+    vals = [d[counter] for d in per_kernel["dispatch"].values() if counter in d]
+    return sum(vals) / len(vals) if vals else None
+
+
+def _run_pass(name, counters, target_args, out):
+    pdir = os.path.join(out, name)
+    os.makedirs(pdir, exist_ok=True)
+    cmd = ["rocprofv3", "--pmc", *counters, "--output-format", "csv", "-d", pdir, "-o", name, "--",
+           sys.executable, "-m", "dense_gemm_12_amd.rocprof_harness", "target", *target_args]
+    print("pass:", " ".join(cmd), flush=True)
+    t0 = time.time()
+    r = subprocess.run(cmd, cwd="/tmp", env={**os.environ, "TMPDIR": "/tmp", "PYTHONPATH": ROOT},
+                       timeout=300)
+    print(f"pass {name}: rc={r.returncode} in {time.time() - t0:.1f}s", flush=True)
+    # rocprofv3 may exit non-zero after a complete run; the CSV decides.
+    return _read_counters(pdir)
+
+
+def _pick(per, want):
+    """The kernel whose name contains `want` with the most dispatches."""
+    best = None
+    for k, v in per.items():
+        if want in k and (best is None or len(v["dispatch"]) > len(per[best]["dispatch"])):
+            best = k
+    return best
+
+
+def run(args):
+    sys.path.insert(0, ROOT)
+    import gemm_inputs as gi
+    out = os.path.abspath(args.out)
+    os.makedirs(out, exist_ok=True)
+    tgt = ["--workload", args.workload, "--iters", str(args.iters)]
+    if args.config:
+        tgt += ["--config", args.config]
+    results = {}
+    for name, counters in PASSES.items():
+        results[name] = _run_pass(name, counters, tgt, out)
+    calib = {}
+    for name in ("fetch", "write"):
+        calib[name] = _run_pass("copy_" + name, PASSES[name], ["--workload", "copy", "--iters", "3"],
+                                out)
+    kname = _pick(results["sq"], "gemm")
+    copy_k = max(calib["fetch"], key=lambda k: len(calib["fetch"][k]["dispatch"]))
+    fetch_copy = _avg(calib["fetch"][copy_k], "FETCH_SIZE")
+    write_copy = _avg(calib["write"][copy_k], "WRITE_SIZE")
+    f_factor = COPY_BYTES / (fetch_copy * 1024) if fetch_copy else None
+    w_factor = COPY_BYTES / (write_copy * 1024) if write_copy else None
+
+    w = gi.WORKLOADS[args.workload]
+    flops = 2.0 * w["M"] * w["N"] * w["K"]
+    sq = results["sq"][kname]
+    gui = _avg(sq, "GRBM_GUI_ACTIVE")
+    mfma = _avg(sq, "SQ_VALU_MFMA_BUSY_CYCLES")
+    valu = _avg(sq, "SQ_ACTIVE_INST_VALU")
+    bank = _avg(sq, "SQ_LDS_BANK_CONFLICT")
+    ldsact = _avg(sq, "SQ_LDS_IDX_ACTIVE")
+    durs = [d["End_Timestamp"] - d["Start_Timestamp"] for d in sq["dispatch"].values()
+            if "End_Timestamp" in d]
+    dur_ns = sorted(durs)[len(durs) // 2] if durs else None
+    # GRBM_GUI_ACTIVE is reported per XCD and summed over the 8 XCDs.
+    gui_cycles = gui / 8 if gui else None
+    fetch_kib = _avg(results["fetch"][_pick(results["fetch"], "gemm")], "FETCH_SIZE")
+    write_kib = _avg(results["write"][_pick(results["write"], "gemm")], "WRITE_SIZE")
+    es = 4 if w["in_dtype"] == "f32" else 2
+    ec = 4 if w["c_dtype"] == "f32" else 2
+    min_bytes = (w["M"] * w["K"] + w["K"] * w["N"]) * es + w["M"] * w["N"] * ec * (2 if w["beta"] else 1)
+    fetch_b = fetch_kib * 1024 * f_factor if (fetch_kib is not None and f_factor) else None
+    write_b = write_kib * 1024 * w_factor if (write_kib is not None and w_factor) else None
+    summary = {
+        "workload": args.workload, "kernel": kname, "config": args.config,
+        "dispatches": len(sq["dispatch"]),
+        "kernel_ns_median_under_pmc": dur_ns,
+        "gui_active_cycles": gui_cycles,
+        "effective_clock_ghz": (gui_cycles / dur_ns) if (gui_cycles and dur_ns) else None,
+        "mfma_util_pct": 100.0 * mfma / (gui_cycles * SIMDS) if (mfma and gui_cycles) else None,
+        "valu_busy_pct": 100.0 * valu * 4 / CUS / gui_cycles if (valu and gui_cycles) else None,
+        "lds_bank_conflict_per_access": bank / (ldsact - bank) if (ldsact and ldsact > bank) else None,
+        "lds_bank_conflict_cycles_pct": 100.0 * bank / (gui_cycles * CUS) if (bank is not None and gui_cycles) else None,
+        "sq_insts_mfma": _avg(sq, "SQ_INSTS_MFMA"), "sq_insts_lds": _avg(sq, "SQ_INSTS_LDS"),
+        "fetch_kib_raw": fetch_kib, "write_kib_raw": write_kib,
+        "copy_calibration": {"bytes_each_way": COPY_BYTES, "fetch_kib": fetch_copy,
+                             "write_kib": write_copy, "fetch_factor": f_factor,
+                             "write_factor": w_factor},
+        "hbm_fetch_bytes": fetch_b, "hbm_write_bytes": write_b,
+        "hbm_bytes_per_launch": (fetch_b + write_b) if (fetch_b is not None and write_b is not None) else None,
+        "min_bytes_per_launch": min_bytes,
+        "flops_per_launch": flops,
+    }
+    if dur_ns:
+        summary["tflops_under_pmc"] = flops / dur_ns / 1e3
+        summary["frac_of_peak_under_pmc"] = summary["tflops_under_pmc"] / PEAK_TFLOPS[w["in_dtype"]]
+        if summary["hbm_bytes_per_launch"]:
+            summary["hbm_gbps"] = summary["hbm_bytes_per_launch"] / dur_ns
+            summary["hbm_frac_of_peak"] = summary["hbm_gbps"] / HBM_GBPS
+    with open(os.path.join(out, "summary.json"), "w") as f:
+        json.dump(summary, f, indent=2)
+    lines = [f"# Counters: {args.workload}", "", f"kernel: `{kname}`", "",
+             "| metric | value |", "|---|---|"]
+    for k, v in summary.items():
+        if isinstance(v, dict):
+            v = json.dumps(v)
+        elif isinstance(v, float):
+            v = f"{v:.4g}"
+        lines.append(f"| {k} | {v} |")
+    with open(os.path.join(out, "summary.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps(summary, indent=2), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="mode", required=True)
+    t = sub.add_parser("target")
+    t.add_argument("--workload", required=True)
+    t.add_argument("--iters", type=int, default=10)
+    t.add_argument("--config", default=None)
+    r = sub.add_parser("run")
+    r.add_argument("--workload", required=True)
+    r.add_argument("--iters", type=int, default=10)
+    r.add_argument("--config", default=None)
+    r.add_argument("--out", required=True)
+    a = ap.parse_args()
+    _target(a) if a.mode == "target" else run(a)
+
+
+if __name__ == "__main__":
+    main()

@@ -82,8 +82,6 @@ def test_every_config_every_layout_integer_bit_exact(in_dtype):
                     name = mg.config_name(in_dtype, cfg)
                     if only_elem_ab and not name.startswith("elemAB"):
                         continue
-                    if name.startswith("dma") and (ta or not tb):
-                        continue  # direct-to-LDS kernels take k-contiguous A and B only
                     what = f"{name} ta={ta} tb={tb} c={c_dtype} {M}x{N}x{K}"
                     log("case " + what)
                     got = run_gpu(A, B, C, alpha=1.5, beta=0.5, ta=ta, tb=tb, c_dtype=c_dtype,
