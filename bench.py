@@ -21,7 +21,6 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import platform
@@ -61,19 +60,6 @@ def min_bytes(w):
     return M * K * es + K * N * es + (M * N * ec if w["beta"] != 0 else 0) + M * N * ec
 
 
-def kernel_src_hash():
-    """Hash of the kernel sources and build flags: counter data taken from an
-    older build no longer describes the current kernels."""
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "dense_gemm_12_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
-    with open(os.path.join(ROOT, "dense_gemm_12_amd", "build.py"), "rb") as fh:
-        h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def load_traffic(config_name, workload):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
@@ -82,6 +68,7 @@ def load_traffic(config_name, workload):
     except (OSError, ValueError):
         return None
     rec = data.get(workload)
+    from dense_gemm_12_amd.srchash import kernel_src_hash
     if not rec or rec.get("config") != config_name or rec.get("src_hash") != kernel_src_hash():
         return None
     return rec.get("hbm_bytes_per_launch")

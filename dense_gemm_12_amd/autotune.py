@@ -1,0 +1,116 @@
+"""Shape-keyed autotuner: times every kernel configuration that can run a
+problem and writes the fastest into the tuning table the library loads
+(``tune_gfx950.txt`` beside the package by default).
+
+    python -m dense_gemm_12_amd.autotune [--out PATH] [--workload NAME ...]
+
+Problems are the named workloads (their own seeded inputs: the data moves
+the chip's clock under MFMA load, so tuning on other data would mislead).
+Each configuration gets a warm-up, then ``--trials`` timed runs of enough
+launches to pass ``--min-ms``, timed with HIP events on the launch stream;
+the median trial decides.  Table rows are
+
+    <in> <c> <ta> <tb> <M> <N> <K> <config>
+
+and the library matches a problem to the nearest row of the same type and
+layout class (log-distance in M, N, K).  The per-configuration timings are
+kept as comments.
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import statistics
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+sys.path.insert(0, ROOT)
+
+
+def time_config(mg, torch, A, B, C, w, cfg, trials, min_ms):
+    stream = torch.cuda.current_stream()
+    call = lambda: mg.gemm(A, B, C, alpha=w["alpha"], beta=w["beta"], trans_a=w["ta"],
+                           trans_b=w["tb"], config=cfg, stream=stream)
+    call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    one = max(e0.elapsed_time(e1), 1e-3)
+    reps = max(5, int(min_ms / one) + 1)
+    for _ in range(3):
+        call()
+    times = []
+    for _ in range(trials):
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / reps)
+    return statistics.median(times)
+
+
+def tune(names, out, trials=3, min_ms=20.0, log=print):
+    import torch
+    import dense_gemm_12_amd as mg
+    import gemm_inputs as gi
+    os.environ["MGEMM_NO_TUNE_TABLE"] = "1"  # time configurations, not an older table's picks
+    mg.load()
+    dev = torch.device("cuda:0")
+    lines = ["# dense_gemm_12_amd tuning table for gfx950 (MI355X); written by autotune.py",
+             "# <in> <c> <ta> <tb> <M> <N> <K> <config>; comments: the three fastest candidates"]
+    for name in names:
+        w = gi.WORKLOADS[name]
+        A, B, C = gi.workload_inputs(name)
+        Ad, Bd = A.to(dev), B.to(dev)
+        Cd = (C.to(dev) if C is not None else
+              torch.zeros((w["M"], w["N"]), dtype=gi.DTYPES[w["c_dtype"]], device=dev))
+        results = []
+        for cfg in range(mg.num_configs(w["in_dtype"])):
+            cname = mg.config_name(w["in_dtype"], cfg)
+            try:
+                ms = time_config(mg, torch, Ad, Bd, Cd, w, cfg, trials, min_ms)
+            except mg.MgemmError as e:
+                if e.status != mg.MG_EUNSUPPORTED:
+                    raise
+                continue
+            flops = 2.0 * w["M"] * w["N"] * w["K"]
+            results.append((ms, cname))
+            log(f"{name:28s} {cname:32s} {ms * 1e3:10.1f} us {flops / ms / 1e9:9.1f} TFLOPS")
+        if not results:
+            continue
+        results.sort()
+        best = results[0][1]
+        lines.append(f"# {name}: " + ", ".join(f"{c}={ms * 1e3:.1f}us" for ms, c in results[:3]))
+        lines.append(f"{w['in_dtype']} {w['c_dtype']} {'T' if w['ta'] else 'N'} {'T' if w['tb'] else 'N'} "
+                     f"{w['M']} {w['N']} {w['K']} {best}")
+        del Ad, Bd, Cd
+        torch.cuda.empty_cache()
+    tmp = out + ".tmp"
+    with open(tmp, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    os.replace(tmp, out)
+    log(f"wrote {out}")
+    return out
+
+
+def main():
+    import gemm_inputs as gi
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", default=os.path.join(HERE, "tune_gfx950.txt"))
+    ap.add_argument("--workload", nargs="*", default=list(gi.WORKLOADS))
+    ap.add_argument("--trials", type=int, default=3)
+    ap.add_argument("--min-ms", type=float, default=20.0)
+    a = ap.parse_args()
+    t0 = time.time()
+    tune(a.workload, a.out, a.trials, a.min_ms, log=lambda s: print(s, flush=True))
+    print(f"tuning took {time.time() - t0:.1f}s", flush=True)
+
+
+if __name__ == "__main__":
+    main()

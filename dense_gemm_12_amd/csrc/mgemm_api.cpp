@@ -322,8 +322,16 @@ mg_status mg_load_tune_table(const char *path) {
   std::vector<Rule> rules;
   char line[512];
   bool ok = true;
+  bool continuation = false;  // inside a line longer than the buffer
   while (fgets(line, sizeof line, f)) {
-    if (line[0] == '#' || line[0] == '\n' || line[0] == '\0') continue;
+    const bool whole = strchr(line, '\n') != nullptr || feof(f);
+    const bool skip = continuation || line[0] == '#' || line[0] == '\n' || line[0] == '\0';
+    continuation = !whole;
+    if (skip) continue;
+    if (!whole) {  // a rule never needs this much text
+      ok = false;
+      break;
+    }
     char in[16], c[16], ta[4], tb[4], cfg[128];
     long long M, N, K;
     if (sscanf(line, "%15s %15s %3s %3s %lld %lld %lld %127s", in, c, ta, tb, &M, &N, &K, cfg) != 8) {

@@ -163,8 +163,15 @@ def run(args):
     min_bytes = (w["M"] * w["K"] + w["K"] * w["N"]) * es + w["M"] * w["N"] * ec * (2 if w["beta"] else 1)
     fetch_b = fetch_kib * 1024 * f_factor if (fetch_kib is not None and f_factor) else None
     write_b = write_kib * 1024 * w_factor if (write_kib is not None and w_factor) else None
+    import dense_gemm_12_amd as mg
+    from dense_gemm_12_amd.srchash import kernel_src_hash
+    lib = mg.load()
+    cfg_id = lib.mg_chosen_config(mg.DTYPE_CODES[w["in_dtype"]], mg.DTYPE_CODES[w["c_dtype"]],
+                                  int(w["ta"]), int(w["tb"]), w["M"], w["N"], w["K"])
     summary = {
-        "workload": args.workload, "kernel": kname, "config": args.config,
+        "workload": args.workload, "kernel": kname,
+        "config": args.config or mg.config_name(w["in_dtype"], cfg_id),
+        "src_hash": kernel_src_hash(),
         "dispatches": len(sq["dispatch"]),
         "kernel_ns_median_under_pmc": dur_ns,
         "gui_active_cycles": gui_cycles,

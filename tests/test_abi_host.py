@@ -140,7 +140,7 @@ def test_planner_prefers_big_tiles_for_big_problems(mg):
 def test_tune_table_load_and_reject(mg, tmp_path):
     good = tmp_path / "t.txt"
     name = mg.config_name("f16", 3)
-    good.write_text(f"# comment\nf16 f16 N T 4096 4096 4096 {name}\n")
+    good.write_text("# " + "x" * 2000 + "\n" + f"f16 f16 N T 4096 4096 4096 {name}\n")
     mg.load_tune_table(str(good))
     assert mg.load().mg_tune_table_size() == 1
     assert mg.chosen_config("f16", "f16", 0, 1, 4096, 4096, 4096) == 3
