@@ -1,0 +1,38 @@
+"""The benchmark's work model against the worked lower-bound example the
+worklog prints (tests/golden/worklog_lower_bound_4092.txt)."""
+import os
+
+import bench
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worklog_lower_bound_4092.txt")
+
+
+def load():
+    vals = {}
+    for line in open(GOLDEN, encoding="utf-8"):
+        if line.startswith("#") or not line.strip():
+            continue
+        k, v = line.split()
+        vals[k] = float(v)
+    return vals
+
+
+def test_flops_and_bytes_match_the_worklog_lower_bounds():
+    g = load()
+    n = int(g["n"])
+    w = dict(M=n, N=n, K=n, in_dtype="f32", c_dtype="f32", beta=0.5)
+    flops = bench.flops(w)                       # 2MNK, the beta add excluded
+    assert round((flops + n * n) / 1e9) == g["flops_incl_beta_add_gflop"]
+    total = bench.min_bytes(w)
+    write = n * n * 4
+    assert round((total - write) / 1e6) == g["min_read_mb"]
+    assert round(write / 1e6) == g["min_write_mb"]
+    assert round(total / 1e6) == g["min_total_mb"]
+    # the page truncates 4.57 ms to 4.5 and 0.349 ms to 0.34
+    assert abs(flops / 30e12 * 1e3 - g["compute_ms_at_30tflops"]) < 0.1
+    assert abs(total / 768e9 * 1e3 - g["memory_ms_at_768gbs"]) < 0.01
+
+
+def test_beta_zero_reads_no_c():
+    w = dict(M=64, N=32, K=16, in_dtype="f16", c_dtype="f16", beta=0.0)
+    assert bench.min_bytes(w) == (64 * 16 + 16 * 32) * 2 + 64 * 32 * 2
