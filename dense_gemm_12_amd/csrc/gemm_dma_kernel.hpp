@@ -58,37 +58,53 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// One operand slice (R rows of the operand x BK values of k) in LDS.
+// One operand slice (R rows of the operand x BK values of k, ES-byte
+// elements) in LDS.  V = 16 / ES elements make one 16-byte chunk; a "k-step"
+// is the 64 bytes of k that the four 16-lane groups of a wave cover with one
+// chunk each (32 k of 16-bit data, 16 k of fp32).
 //
-// KC = true, k contiguous in memory: LDS rows are operand rows of BK*2
+// KC = true, k contiguous in memory: LDS rows are operand rows of BK*ES
 // bytes; 16-byte chunk c of row r sits at slot c ^ swz(r), swz(r) = r mod 8
 // (128-byte rows) or (r / 2) mod 4 (64-byte rows).  Lane l's fragment for
 // 16-row block b, k-step ks is row 16b + l%16, chunk 4ks + l/16: one
-// ds_read_b128.
+// ds_read_b128 (for fp32 its four floats are the four k sub-steps
+// 4(l/16) + s of the k-step).
 //
 // KC = false, operand rows contiguous in memory: LDS rows are the BK k
-// values, each R*2 bytes; chunk c of k-row k sits at slot c ^ swz(k),
-// swz(k) = 2 * ((k mod 4) | ((k / 8) mod 2) * 4), an even value so the two
-// 16-byte chunks of each 32-byte span stay adjacent.  ds_read_b64_tr_b16
-// returns to lane j of a 16-lane group element j%4 of the 8-byte reads of
-// lanes j/4, j/4+4, j/4+8, j/4+12 of the group; so lane i of group g reads
-// k-row 8g + 4h + i/4 at columns 16b + 4(i%4) .. +3 and receives, for its own
-// column 16b + j, the four k values 8g + 4h .. +3.  Two reads (h = 0, 1)
-// give the 8 k values of the MFMA operand.
-template <int R, int BK, bool KC, int NW>
+// values, each R*ES bytes.
+//   16-bit: chunk c of k-row k sits at slot c ^ swz(k), swz(k) = 2 * ((k mod
+//   4) | ((k / 8) mod 2) * 4), an even value so the two 16-byte chunks of
+//   each 32-byte span stay adjacent.  ds_read_b64_tr_b16 returns to lane j of
+//   a 16-lane group element j%4 of the 8-byte reads of lanes j/4, j/4+4,
+//   j/4+8, j/4+12 of the group; so lane i of group g reads k-row 8g + 4h +
+//   i/4 at columns 16b + 4(i%4) .. +3 and receives, for its own column 16b +
+//   j, the four k values 8g + 4h .. +3.  Two reads (h = 0, 1) give the 8 k
+//   values of the MFMA operand.
+//   fp32: no permutation.  Read number r = 4q + s of a k-step has lane j of
+//   group g load k-row 16ks + 4g + s at operand rows 64q + 4j .. +3 (one
+//   aligned 256-byte span per 16-lane group, so conflict-free); float t of it
+//   is the sub-step-s value of 16-row block 4q + t, whose lane-j row is
+//   64q + 4j + t.  The tile therefore orders the rows of each 64-row quad as
+//   (4j + t), and the epilogue maps them back.
+template <int R, int BK, bool KC, int NW, int ES = 2>
 struct DmaOperand {
-  static constexpr int BYTES = R * BK * 2;
+  static constexpr int V = 16 / ES;
+  static constexpr int BYTES = R * BK * ES;
   static constexpr int INST = BYTES / 1024 / NW;  // DMA instructions per wave per slice
-  static constexpr int ROWB = KC ? BK * 2 : R * 2;
+  static constexpr int ROWB = KC ? BK * ES : R * ES;
   static constexpr int CPR = ROWB / 16;
   static constexpr int RPB = 1024 / ROWB;         // LDS rows per 1 KiB DMA block
-  static constexpr int READS = KC ? 1 : 2;        // LDS reads per 16-row fragment
+  static constexpr int READS = (KC || ES == 4) ? 1 : 2;  // LDS reads per fragment register
+  static constexpr int KSTEP = 64 / ES;           // k values per k-step
+  static_assert(ES == 2 || ES == 4, "16-bit or fp32 elements");
   static_assert(BYTES % (1024 * NW) == 0, "whole DMA blocks per wave");
-  static_assert(KC ? (CPR == 4 || CPR == 8) : (CPR >= 16), "supported LDS row widths");
+  static_assert(KC ? (CPR == 4 || CPR == 8) : (CPR >= 16 && 1024 % ROWB == 0),
+                "supported LDS row widths");
 
   static __device__ __forceinline__ int swz(int row) {
     if constexpr (KC) return CPR == 8 ? (row & 7) : ((row >> 1) & 3);
-    else return 2 * ((row & 3) | (((row >> 3) & 1) << 2));
+    else if constexpr (ES == 2) return 2 * ((row & 3) | (((row >> 3) & 1) << 2));
+    else return 0;
   }
 
   // DMA instruction u of this wave for one slice.  rs: buffer at the stored
@@ -99,17 +115,19 @@ struct DmaOperand {
     const int blk = wave * INST + u;
     const int row = blk * RPB + lane / CPR;
     const int c = (lane % CPR) ^ swz(row);
-    const bool ok = KC ? (row < rv && c * 8 < kv) : (row < kv && c * 8 < rv);
+    const bool ok = KC ? (row < rv && c * V < kv) : (row < kv && c * V < rv);
     const uint32_t off = ok ? row * ldb + c * 16 : kOOB;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + blk * 1024), 16, off, 0, 0, 0);
   }
 
   // Per-lane fragment addressing.  rowblk0: first 16-row block of the wave
-  // within the slice; NB: blocks per wave; KSTEPS: k-steps per slice.
+  // within the slice; NB: fragment registers per k-step (16-row blocks; for
+  // fp32 k-major, reads 4q + s); KSTEPS: k-steps per slice.
   template <int NB, int KSTEPS>
   struct Frag {
+    static constexpr bool TR16 = !KC && ES == 2;
     int base;
-    int xo[KC ? KSTEPS : NB];
+    int xo[KC ? KSTEPS : (TR16 ? NB : 1)];
 
     __device__ __forceinline__ void init(int lane, int rowblk0) {
       const int j = lane & 15, g = lane >> 4;
@@ -117,19 +135,23 @@ struct DmaOperand {
         base = (rowblk0 * 16 + j) * ROWB;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) xo[ks] = ((ks * 4 + g) ^ swz(j)) * 16;
-      } else {
+      } else if constexpr (TR16) {
         const int gk = 2 * ((j >> 2) | ((g & 1) << 2));  // swz of the lane's k-row
         base = (8 * g + (j >> 2)) * ROWB + 8 * (j & 1);
 #pragma unroll
         for (int b = 0; b < NB; ++b) xo[b] = ((((rowblk0 + b) * 2) ^ gk) + ((j >> 1) & 1)) * 16;
+      } else {
+        static_assert(KC || TR16 || NB % 4 == 0, "fp32 k-major fragments come in 64-row quads");
+        base = 4 * g * ROWB + rowblk0 * 16 * ES + 16 * j;
+        xo[0] = 0;
       }
     }
 
-    // Read number h (0 .. READS-1) of fragment (block b, k-step ks) into f.
+    // Read number h (0 .. READS-1) of fragment register b, k-step ks, into f.
     __device__ __forceinline__ void read(const char *st, int b, int ks, int h, u32x4 &f) const {
       if constexpr (KC) {
         f = *reinterpret_cast<const u32x4 *>(st + base + b * 16 * ROWB + xo[ks]);
-      } else {
+      } else if constexpr (TR16) {
         const char *pa = st + base + (ks * 32 + 4 * h) * ROWB + xo[b];
         const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) i16x4 *)((__attribute__((address_space(3))) char *)pa));
@@ -141,6 +163,8 @@ struct DmaOperand {
           f.z = w.x;
           f.w = w.y;
         }
+      } else {
+        f = *reinterpret_cast<const u32x4 *>(st + base + (ks * KSTEP + (b & 3)) * ROWB + (b >> 2) * 256);
       }
     }
   };
@@ -151,17 +175,24 @@ template <typename TI, typename TO, int BM_, int BN_, int BK_, int STAGES_, int 
 struct DmaTile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
   static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
-  using OA = DmaOperand<BM, BK, A_KC, NW>;
-  using OB = DmaOperand<BN, BK, B_KC, NW>;
+  static constexpr int ES = sizeof(TI);
+  using OA = DmaOperand<BM, BK, A_KC, NW, ES>;
+  using OB = DmaOperand<BN, BK, B_KC, NW, ES>;
   static constexpr int A_BYTES = OA::BYTES, B_BYTES = OB::BYTES;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int A_INST = OA::INST, B_INST = OB::INST;
   static constexpr int LOADS_PER_SLICE = A_INST + B_INST;
   static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
   static constexpr int MI = WTM / 16, NJ = WTN / 16;
-  static constexpr int KSTEPS = BK / 32;           // 16x16x32 MFMA k-steps per slice
+  static constexpr int KSTEPS = BK * ES / 64;      // k-steps (64 bytes of k) per slice
   static constexpr int RD_B = NJ * OB::READS, RD_A = MI * OA::READS;
-  static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
+  // MFMA instructions per k-step: one 16x16x32 per block pair for 16-bit
+  // inputs, four 16x16x4 (sub-steps s) for fp32.
+  static constexpr int SUB = Mfma<TI>::kInsts;
+  static constexpr int MFMAS = MI * NJ * SUB;
+  // fp32 k-major operands order the rows of each 64-row quad as 4j + t.
+  static constexpr bool A_Q = ES == 4 && !A_KC, B_Q = ES == 4 && !B_KC;
+  static_assert(KSTEPS == 1 || KSTEPS == 2, "one or two k-steps per slice");
   static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS budget");
   static_assert(LOADS_PER_SLICE * (STAGES - 1) < 64, "vmcnt range");
 
@@ -177,11 +208,11 @@ struct DmaTile {
     const int m0 = tm * BM, n0 = tn * BN;
     // Slice origins advance by BK along k: BK elements for a k-contiguous
     // operand, BK rows for a k-major one.
-    const char *Ab = static_cast<const char *>(p.A) + (A_KC ? (int64_t)m0 * p.lda : m0) * 2;
-    const char *Bb = static_cast<const char *>(p.B) + (B_KC ? (int64_t)n0 * p.ldb : n0) * 2;
-    const int64_t a_step = (A_KC ? BK : (int64_t)BK * p.lda) * 2;
-    const int64_t b_step = (B_KC ? BK : (int64_t)BK * p.ldb) * 2;
-    const uint32_t lda_b = (uint32_t)(p.lda * 2), ldb_b = (uint32_t)(p.ldb * 2);
+    const char *Ab = static_cast<const char *>(p.A) + (A_KC ? (int64_t)m0 * p.lda : m0) * ES;
+    const char *Bb = static_cast<const char *>(p.B) + (B_KC ? (int64_t)n0 * p.ldb : n0) * ES;
+    const int64_t a_step = (A_KC ? BK : (int64_t)BK * p.lda) * ES;
+    const int64_t b_step = (B_KC ? BK : (int64_t)BK * p.ldb) * ES;
+    const uint32_t lda_b = (uint32_t)(p.lda * ES), ldb_b = (uint32_t)(p.ldb * ES);
     const int rva = p.M - m0, rvb = p.N - n0;
     const int nk = (p.K + BK - 1) / BK;
 
@@ -218,11 +249,21 @@ struct DmaTile {
 #pragma unroll
       for (int t = 0; t < RD_A + RD_B; ++t) read_op(st, ks, t, fa, fb);
     };
+    // MFMA instruction t of a k-step, sub-step-major so that consecutive
+    // instructions never share an accumulator.
+    auto mfma = [&](int t, const u32x4 (&fa)[MI], const u32x4 (&fb)[NJ]) {
+      const int s = t / (MI * NJ), i = (t % (MI * NJ)) / NJ, j = t % NJ;
+      if constexpr (SUB == 1) {
+        Mfma<TI>::step(acc[i][j], fb[j], fa[i]);
+      } else {
+        const float a = __builtin_bit_cast(float, A_Q ? fa[(i & ~3) + s][i & 3] : fa[i][s]);
+        const float b = __builtin_bit_cast(float, B_Q ? fb[(j & ~3) + s][j & 3] : fb[j][s]);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(b, a, acc[i][j], 0, 0, 0);
+      }
+    };
     auto mfmas = [&](const u32x4 (&fa)[MI], const u32x4 (&fb)[NJ]) {
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) Mfma<TI>::step(acc[i][j], fb[j], fa[i]);
+      for (int t = 0; t < MFMAS; ++t) mfma(t, fa, fb);
     };
 
     if constexpr (STAGES == 2 && KSTEPS == 2) {
@@ -237,7 +278,7 @@ struct DmaTile {
       // (With more memory ops than MFMAs, each MFMA is followed by up to
       // ceil(ops / MFMAs) of them.)  The MFMAs never wait on an LDS read; the
       // barrier is the only point where the matrix pipe can drain.
-      constexpr int SLOTS = MI * NJ;
+      constexpr int SLOTS = MFMAS;
       constexpr int PA = (RD_A + RD_B + SLOTS - 1) / SLOTS;                    // ops per MFMA, phase A
       constexpr int PC = (LOADS_PER_SLICE + RD_A + RD_B + SLOTS - 1) / SLOTS;  // ops per MFMA, phase C
       u32x4 fa0[MI], fb0[NJ], fa1[MI], fb1[NJ];
@@ -250,8 +291,8 @@ struct DmaTile {
         const char *st = lds + (kt & 1) * STAGE_BYTES;
         const char *nx = lds + ((kt + 1) & 1) * STAGE_BYTES;
 #pragma unroll
-        for (int t = 0; t < MI * NJ; ++t) {  // phase A
-          Mfma<TI>::step(acc[t / NJ][t % NJ], fb0[t % NJ], fa0[t / NJ]);
+        for (int t = 0; t < SLOTS; ++t) {  // phase A
+          mfma(t, fa0, fb0);
 #pragma unroll
           for (int o = t * PA; o < (t + 1) * PA; ++o)
             if (o < RD_A + RD_B) read_op(st, 1, o, fa1, fb1);
@@ -261,8 +302,8 @@ struct DmaTile {
         wait_lgkm0();  // this wave's reads of S are done
         __syncthreads();
 #pragma unroll
-        for (int t = 0; t < MI * NJ; ++t) {  // phase C
-          Mfma<TI>::step(acc[t / NJ][t % NJ], fb1[t % NJ], fa1[t / NJ]);
+        for (int t = 0; t < SLOTS; ++t) {  // phase C
+          mfma(t, fa1, fb1);
 #pragma unroll
           for (int o = t * PC; o < (t + 1) * PC; ++o) {
             if (o < LOADS_PER_SLICE) dma_op(kt + 2, o);
@@ -279,7 +320,7 @@ struct DmaTile {
       // read by every wave before the previous barrier).  The barrier at the
       // end of slice kt waits only for slice kt+2, so STAGES-1 slices of DMA
       // stay in flight.
-      constexpr int SLOTS = MI * NJ;
+      constexpr int SLOTS = MFMAS;
       constexpr int PO = (LOADS_PER_SLICE + RD_A + RD_B + SLOTS - 1) / SLOTS;  // ops per MFMA
       u32x4 fa[2][MI], fb[2][NJ];
 #pragma unroll
@@ -297,8 +338,8 @@ struct DmaTile {
           const int k = kt + h;
           const char *nx = lds + ((k + 1) % STAGES) * STAGE_BYTES;
 #pragma unroll
-          for (int t = 0; t < MI * NJ; ++t) {
-            Mfma<TI>::step(acc[t / NJ][t % NJ], fb[h][t % NJ], fa[h][t / NJ]);
+          for (int t = 0; t < SLOTS; ++t) {
+            mfma(t, fa[h], fb[h]);
 #pragma unroll
             for (int o = t * PO; o < (t + 1) * PO; ++o) {
               if (o < RD_A + RD_B) read_op(nx, 0, o, fa[h ^ 1], fb[h ^ 1]);
@@ -333,7 +374,7 @@ struct DmaTile {
     }
 
     wait_vmcnt<0>();  // the trailing (all out-of-range) DMA has landed before the LDS is released
-    GemmEpilogue<TO, MI, NJ>::store(p, acc, m0 + wm * WTM, n0 + wn * WTN, lane);
+    GemmEpilogue<TO, MI, NJ, A_Q, B_Q>::store(p, acc, m0 + wm * WTM, n0 + wn * WTN, lane);
   }
 };
 

@@ -15,6 +15,12 @@ Two modes:
     runs the library's GEMM ``iters`` times; ``--workload copy`` instead runs a
     1 GiB device-to-device copy (the calibration kernel).
 
+``python -m dense_gemm_12_amd.rocprof_harness collect DIR [DIR ...] [--profiles profiles]``
+    Copies each run's summary into ``profiles/counters_<workload>.md`` and
+    records its calibrated HBM traffic, kernel configuration and kernel
+    source hash in ``profiles/traffic.json`` (the file the benchmark reads its
+    ``traffic`` figure from, valid only while hash and configuration match).
+
 The driver never touches the GPU itself; each pass is a fresh process started
 directly by rocprofv3.
 """
@@ -169,7 +175,7 @@ def run(args):
     cfg_id = lib.mg_chosen_config(mg.DTYPE_CODES[w["in_dtype"]], mg.DTYPE_CODES[w["c_dtype"]],
                                   int(w["ta"]), int(w["tb"]), w["M"], w["N"], w["K"])
     summary = {
-        "workload": args.workload, "kernel": kname,
+        "workload": args.workload, "kernel": kname, "iters": args.iters,
         "config": args.config or mg.config_name(w["in_dtype"], cfg_id),
         "src_hash": kernel_src_hash(),
         "dispatches": len(sq["dispatch"]),
@@ -211,6 +217,47 @@ def run(args):
     print(json.dumps(summary, indent=2), flush=True)
 
 
+def collect(dirs, profiles):
+    path = os.path.join(profiles, "traffic.json")
+    table = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            table = json.load(f)
+    for d in dirs:
+        with open(os.path.join(d, "summary.json")) as f:
+            s = json.load(f)
+        w = s["workload"]
+        cal = s["copy_calibration"]
+        table[w] = {"config": s["config"], "src_hash": s["src_hash"],
+                    "hbm_bytes_per_launch": s["hbm_bytes_per_launch"],
+                    "hbm_fetch_bytes": s["hbm_fetch_bytes"], "hbm_write_bytes": s["hbm_write_bytes"],
+                    "fetch_factor": cal["fetch_factor"], "write_factor": cal["write_factor"],
+                    "source": f"profiles/counters_{w}.md"}
+        with open(os.path.join(d, "summary.md")) as f:
+            body = f.read().split("\n", 1)[1]
+        cmd = (f"python3 -m dense_gemm_12_amd.rocprof_harness run --workload {w} --iters "
+               f"{s.get('iters', 5)} --out gpurun_out/harness_{w}")
+        text = (f"# Hardware counters: {w}\n\n"
+                "Command (each counter group is one rocprofv3 --pmc pass over the workload, plus two "
+                "passes over a 1 GiB copy for calibrating FETCH_SIZE/WRITE_SIZE):\n\n"
+                f"```\n{cmd}\n```\n\nKernel configuration `{s['config']}`, kernel source hash "
+                f"`{s['src_hash']}`.\n{body}\n"
+                f"Calibration: a {cal['bytes_each_way']} B device copy reads FETCH_SIZE = "
+                f"{cal['fetch_kib']:.0f} KiB and WRITE_SIZE = {cal['write_kib']:.0f} KiB, so fetched "
+                f"bytes = FETCH_SIZE x 1024 x {cal['fetch_factor']:.4f} and written bytes = WRITE_SIZE "
+                f"x 1024 x {cal['write_factor']:.4f}.\n"
+                "FETCH_SIZE counts L2 misses (requests that leave the XCD's L2 for the Infinity Cache "
+                "/ HBM); with the 256 MB Infinity Cache some of these are not DRAM reads.\n"
+                "GRBM_GUI_ACTIVE covers a little time around each dispatch, so for short kernels "
+                "(about 100 us) the effective clock reads high and the MFMA utilisation low.\n")
+        with open(os.path.join(profiles, f"counters_{w}.md"), "w") as f:
+            f.write(text)
+        print(f"{w}: {s['config']} {s['hbm_bytes_per_launch']:.4g} B/launch")
+    with open(path, "w") as f:
+        json.dump(table, f, indent=2)
+        f.write("\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -223,8 +270,16 @@ def main():
     r.add_argument("--iters", type=int, default=10)
     r.add_argument("--config", default=None)
     r.add_argument("--out", required=True)
+    c = sub.add_parser("collect")
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--profiles", default=os.path.join(ROOT, "profiles"))
     a = ap.parse_args()
-    _target(a) if a.mode == "target" else run(a)
+    if a.mode == "target":
+        _target(a)
+    elif a.mode == "run":
+        run(a)
+    else:
+        collect(a.dirs, a.profiles)
 
 
 if __name__ == "__main__":
