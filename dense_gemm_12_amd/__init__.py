@@ -26,7 +26,7 @@ DTYPE_CODES = {"f32": MG_F32, "f16": MG_F16, "bf16": MG_BF16}
 # Every exported symbol of include/mgemm.h.
 EXPORTS = (
     "gemm_f32", "gemm_f16", "gemm_bf16", "gemm_f32_cfg", "gemm_f16_cfg", "gemm_bf16_cfg",
-    "mg_num_configs", "mg_config_name", "mg_chosen_config", "mg_load_tune_table",
+    "gemm_ex", "mg_workspace_size", "mg_num_configs", "mg_config_name", "mg_chosen_config", "mg_load_tune_table",
     "mg_tune_table_size", "mg_status_str", "mg_last_hip_error", "mg_version",
 )
 
@@ -65,6 +65,11 @@ def load(path: str | None = None):
         for name in ("gemm_f32", "gemm_f16", "gemm_bf16", "gemm_f32_cfg", "gemm_f16_cfg",
                      "gemm_bf16_cfg"):
             getattr(lib, name).restype = ci
+        lib.gemm_ex.argtypes = [ci, ci, ci, ci, i64, i64, i64, f, vp, i64, vp, i64, f, vp, i64, vp,
+                                ctypes.c_size_t, ci, ci, vp]
+        lib.gemm_ex.restype = ci
+        lib.mg_workspace_size.argtypes = [ci, ci, ci, ci, i64, i64, i64, i64, i64]
+        lib.mg_workspace_size.restype = ctypes.c_size_t
         lib.mg_num_configs.argtypes = [ci]
         lib.mg_num_configs.restype = ci
         lib.mg_config_name.argtypes = [ci, ci]
@@ -125,6 +130,17 @@ def gemm_bf16_cfg(config, ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_typ
                                 ldc, stream), "gemm_bf16_cfg")
 
 
+def gemm_ex(in_type, c_type, ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+            workspace_bytes, config=-1, splits=0, stream=None):
+    _check(load().gemm_ex(in_type, c_type, ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                          workspace, workspace_bytes, config, splits, stream), "gemm_ex")
+
+
+def workspace_size(in_type, c_type, ta, tb, M, N, K, lda, ldb) -> int:
+    """Bytes of split-K workspace gemm_ex(splits=0) uses (codes as in the C ABI)."""
+    return load().mg_workspace_size(in_type, c_type, ta, tb, M, N, K, lda, ldb)
+
+
 def num_configs(in_type: str) -> int:
     return load().mg_num_configs(DTYPE_CODES[in_type])
 
@@ -160,13 +176,17 @@ def _ld(t) -> int:
 
 
 def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, trans_a: bool = False,
-         trans_b: bool = False, config: int = -1, stream=None):
+         trans_b: bool = False, config: int = -1, stream=None, workspace=None, splits: int = 0):
     """C <- alpha * op(A) @ op(B) + beta * C on C's device, in place.
 
     A, B, C are 2-D CUDA tensors holding the *stored* matrices (A is K x M when
     trans_a; B is N x K when trans_b).  Input dtypes: float32, float16 or
     bfloat16 (A and B alike); C is float32 or the input dtype.  Runs on the
     current stream unless ``stream`` (a torch.cuda.Stream) is given.
+
+    With ``workspace`` (a CUDA tensor used as raw bytes, see
+    ``workspace_size``) the call goes through ``gemm_ex`` and may split K
+    (``splits``: 0 = the planner's choice, 1 = never, n = that many ranges).
     """
     import torch
     if A.dtype != B.dtype:
@@ -180,6 +200,15 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, trans_a: bool = False,
     s = (stream or torch.cuda.current_stream(C.device)).cuda_stream
     ta, tb = (MG_T if trans_a else MG_N), (MG_T if trans_b else MG_N)
     args = (M, N, K, float(alpha), A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), float(beta))
+    if workspace is not None or splits not in (0, 1):
+        codes = {torch.float32: MG_F32, torch.float16: MG_F16, torch.bfloat16: MG_BF16}
+        if A.dtype not in codes or C.dtype not in codes:
+            raise TypeError(f"unsupported dtypes {A.dtype} -> {C.dtype}")
+        wp = workspace.data_ptr() if workspace is not None else None
+        wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        gemm_ex(codes[A.dtype], codes[C.dtype], ta, tb, *args, C.data_ptr(), _ld(C), wp, wb,
+                config, splits, s)
+        return C
     if A.dtype == torch.float32:
         if C.dtype != torch.float32:
             raise TypeError("fp32 GEMM writes fp32 C")

@@ -9,6 +9,20 @@
 
 namespace mg {
 
+// Split-K: the epilogue of split s writes the raw fp32 sum (alpha = 1,
+// beta = 0) to its slab of the workspace, rows of N floats.  kb is the
+// split's first k.
+__device__ __forceinline__ GemmParams partial_params(const GemmParams &p, int kb) {
+  GemmParams q = p;
+  const int s = kb / p.k_chunk;
+  q.C = p.ws + (int64_t)s * p.M * p.N;
+  q.ldc = p.N;
+  q.alpha = 1.0f;
+  q.beta = 0.0f;
+  q.c_vec = (p.N % 4) == 0;
+  return q;
+}
+
 // Accumulator layout: acc[i][j] is the 16x16 block (i, j) of the wave's
 // sub-tile and lane l holds its element (row position l%16, column positions
 // 4*(l/16) + v, v = 0..3).  Positions map to C as follows.

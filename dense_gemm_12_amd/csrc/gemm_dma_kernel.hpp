@@ -202,23 +202,24 @@ struct DmaTile {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-    int tm, tn;
-    tile_coords(remap_xcd(blockIdx.x, p.tiles_m * p.tiles_n), p.tiles_m, p.tiles_n, p.group_m, tm,
-                tn);
+    int tm, tn, kb, K;
+    work_coords(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, p.splits, p.K, p.k_chunk, tm, tn, kb, K);
     const int m0 = tm * BM, n0 = tn * BN;
     // Slice origins advance by BK along k: BK elements for a k-contiguous
     // operand, BK rows for a k-major one.
-    const char *Ab = static_cast<const char *>(p.A) + (A_KC ? (int64_t)m0 * p.lda : m0) * ES;
-    const char *Bb = static_cast<const char *>(p.B) + (B_KC ? (int64_t)n0 * p.ldb : n0) * ES;
+    const char *Ab = static_cast<const char *>(p.A) +
+                     (A_KC ? (int64_t)m0 * p.lda + kb : (int64_t)kb * p.lda + m0) * ES;
+    const char *Bb = static_cast<const char *>(p.B) +
+                     (B_KC ? (int64_t)n0 * p.ldb + kb : (int64_t)kb * p.ldb + n0) * ES;
     const int64_t a_step = (A_KC ? BK : (int64_t)BK * p.lda) * ES;
     const int64_t b_step = (B_KC ? BK : (int64_t)BK * p.ldb) * ES;
     const uint32_t lda_b = (uint32_t)(p.lda * ES), ldb_b = (uint32_t)(p.ldb * ES);
     const int rva = p.M - m0, rvb = p.N - n0;
-    const int nk = (p.K + BK - 1) / BK;
+    const int nk = (K + BK - 1) / BK;
 
     auto dma_op = [&](int kt, int u) {  // DMA instruction u (A first, then B) of slice kt
       char *st = lds + (kt % STAGES) * STAGE_BYTES;
-      const int kv = p.K - kt * BK;
+      const int kv = K - kt * BK;
       if (u < A_INST)
         OA::dma(make_rsrc(Ab + kt * a_step), lda_b, rva, kv, st, wave, lane, u);
       else
@@ -374,7 +375,11 @@ struct DmaTile {
     }
 
     wait_vmcnt<0>();  // the trailing (all out-of-range) DMA has landed before the LDS is released
-    GemmEpilogue<TO, MI, NJ, A_Q, B_Q>::store(p, acc, m0 + wm * WTM, n0 + wn * WTN, lane);
+    if (p.splits > 1)
+      GemmEpilogue<float, MI, NJ, A_Q, B_Q>::store(partial_params(p, kb), acc, m0 + wm * WTM, n0 + wn * WTN,
+                                                   lane);
+    else
+      GemmEpilogue<TO, MI, NJ, A_Q, B_Q>::store(p, acc, m0 + wm * WTM, n0 + wn * WTN, lane);
   }
 };
 

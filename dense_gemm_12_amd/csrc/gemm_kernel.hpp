@@ -218,9 +218,8 @@ struct GemmTile {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-    int tm, tn;
-    tile_coords(remap_xcd(blockIdx.x, p.tiles_m * p.tiles_n), p.tiles_m, p.tiles_n, p.group_m, tm,
-                tn);
+    int tm, tn, kb, K;
+    work_coords(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, p.splits, p.K, p.k_chunk, tm, tn, kb, K);
     const int m0 = tm * BM, n0 = tn * BN;
 
     f32x4 acc[MI][NJ];
@@ -232,23 +231,23 @@ struct GemmTile {
     const char *Ab = static_cast<const char *>(p.A);
     const char *Bb = static_cast<const char *>(p.B);
     const uint32_t lda_b = (uint32_t)(p.lda * ES), ldb_b = (uint32_t)(p.ldb * ES);
-    const int nk = (p.K + BK - 1) / BK;
+    const int nk = (K + BK - 1) / BK;
 
     // Origin of slice kt for each operand (bytes).
     auto a_slice = [&](int kt) -> const char * {
-      const int64_t k0 = (int64_t)kt * BK;
+      const int64_t k0 = (int64_t)kb + (int64_t)kt * BK;
       return A_KC ? Ab + ((int64_t)m0 * p.lda + k0) * ES : Ab + (k0 * p.lda + m0) * ES;
     };
     auto b_slice = [&](int kt) -> const char * {
-      const int64_t k0 = (int64_t)kt * BK;
+      const int64_t k0 = (int64_t)kb + (int64_t)kt * BK;
       return B_KC ? Bb + ((int64_t)n0 * p.ldb + k0) * ES : Bb + (k0 * p.ldb + n0) * ES;
     };
 
     LA la;
     LB lb;
     if (nk > 0) {
-      la.load(a_slice(0), lda_b, p.M - m0, p.K, tid);
-      lb.load(b_slice(0), ldb_b, p.N - n0, p.K, tid);
+      la.load(a_slice(0), lda_b, p.M - m0, K, tid);
+      lb.load(b_slice(0), ldb_b, p.N - n0, K, tid);
       la.store(lds, tid);
       lb.store(lds + BM * PITCH, tid);
     }
@@ -259,7 +258,7 @@ struct GemmTile {
       char *nxt = lds + ((kt + 1) & 1) * STAGE_BYTES;
       const bool more = kt + 1 < nk;
       if (more) {
-        const int kv = p.K - (kt + 1) * BK;
+        const int kv = K - (kt + 1) * BK;
         la.load(a_slice(kt + 1), lda_b, p.M - m0, kv, tid);
         lb.load(b_slice(kt + 1), ldb_b, p.N - n0, kv, tid);
       }
@@ -271,7 +270,10 @@ struct GemmTile {
       __syncthreads();
     }
 
-    GemmEpilogue<TO, MI, NJ>::store(p, acc, m0 + wm * WTM, n0 + wn * WTN, lane);
+    if (p.splits > 1)
+      GemmEpilogue<float, MI, NJ>::store(partial_params(p, kb), acc, m0 + wm * WTM, n0 + wn * WTN, lane);
+    else
+      GemmEpilogue<TO, MI, NJ>::store(p, acc, m0 + wm * WTM, n0 + wn * WTN, lane);
   }
 
 };
@@ -294,6 +296,37 @@ __global__ void __launch_bounds__(256) scale_c_kernel(GemmParams p) {
     // alpha * (empty or ignored product) contributes +0: 0 + beta*C (so a
     // -0 product beta*C becomes +0, as in the formula's left-to-right sum).
     *c = from_f32<TO>(p.beta == 0.0f ? 0.0f : 0.0f + p.beta * to_f32(*c));
+  }
+}
+
+// Split-K reduction: C = alpha * (P_0 + P_1 + ... + P_{S-1}) + beta * C with
+// the partials summed in split order, so the result does not depend on
+// which split finished first; one rounding to the C type, and beta == 0
+// never reads C.  Each thread owns 4 consecutive columns of one row.
+template <typename TO>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmParams p) {
+  const int64_t slab = (int64_t)p.M * p.N;
+  const int ng = (p.N + 3) / 4;
+  const int64_t total = (int64_t)p.M * ng;
+  const bool use_beta = p.beta != 0.0f;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
+       g += (int64_t)gridDim.x * blockDim.x) {
+    const int m = (int)(g / ng), n = (int)(g - (int64_t)m * ng) * 4;
+    const float *w = p.ws + (int64_t)m * p.N + n;
+    float x[4] = {0.f, 0.f, 0.f, 0.f};
+    if ((p.N & 3) == 0) {
+      for (int s = 0; s < p.splits; ++s) {
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(w + s * slab);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] += v[e];
+      }
+    } else {
+      for (int s = 0; s < p.splits; ++s)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < p.N) x[e] += w[s * slab + e];
+    }
+    GemmEpilogue<TO, 1, 1>::store4(p, static_cast<TO *>(p.C) + (int64_t)m * p.ldc, n, x, use_beta);
   }
 }
 

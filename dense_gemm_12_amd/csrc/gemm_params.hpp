@@ -16,6 +16,14 @@ struct GemmParams {
   int tiles_m, tiles_n;   // grid = tiles_m * tiles_n workgroups
   int group_m;            // tile-rows per raster group
   int c_vec;              // C rows allow 16-byte (fp32) / 8-byte (16-bit) access
+  // Split-K.  splits == 1: one workgroup per tile covers all of K and the
+  // epilogue writes C.  splits > 1: the grid is tiles * splits, split s
+  // covers k in [s * k_chunk, min(K, (s + 1) * k_chunk)) and writes its fp32
+  // partial tile to ws + s * M * N (row pitch N); a reduction kernel then
+  // sums the partials in split order and applies alpha and beta.
+  int splits;
+  int k_chunk;            // multiple of every tile's BK
+  float *ws;
 };
 
 typedef hipError_t (*LaunchFn)(const GemmParams &, hipStream_t);
@@ -38,6 +46,7 @@ const KernelEntry *entries_f32(int *n);
 const KernelEntry *entries_f16(int *n);
 const KernelEntry *entries_bf16(int *n);
 
-LaunchFn scale_launcher(int c_dtype);  // 0 = f32, 1 = f16, 2 = bf16
+LaunchFn scale_launcher(int c_dtype);   // 0 = f32, 1 = f16, 2 = bf16
+LaunchFn reduce_launcher(int c_dtype);  // split-K partial sums -> C, same codes
 
 }  // namespace mg

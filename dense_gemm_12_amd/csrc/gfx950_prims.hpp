@@ -96,6 +96,20 @@ __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int
   tn = in_g / gsz;
 }
 
+// Workgroup -> (tile row, tile column, K range).  The launch covers
+// tiles * splits workgroups; the split index is the slow one, so each XCD's
+// contiguous share of logical indices holds whole splits, whose workgroups
+// read the same K range of A and B.
+__device__ __forceinline__ void work_coords(int b, int tiles_m, int tiles_n, int group_m, int splits,
+                                            int K, int k_chunk, int &tm, int &tn, int &k0, int &kl) {
+  const int tiles = tiles_m * tiles_n;
+  const int l = remap_xcd(b, tiles * splits);
+  const int s = l / tiles;
+  tile_coords(l - s * tiles, tiles_m, tiles_n, group_m, tm, tn);
+  k0 = s * k_chunk;
+  kl = splits > 1 ? min(K - k0, k_chunk) : K;
+}
+
 // ------------------------------------------------------------ conversions --
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }

@@ -36,6 +36,23 @@ static hipError_t launch_scale(const GemmParams &p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename TO>
+static hipError_t launch_reduce(const GemmParams &p, hipStream_t s) {
+  const int64_t total = (int64_t)p.M * ((p.N + 3) / 4);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(splitk_reduce_kernel<TO>, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+LaunchFn reduce_launcher(int c_dtype) {
+  switch (c_dtype) {
+    case 0: return &launch_reduce<float>;
+    case 1: return &launch_reduce<_Float16>;
+    default: return &launch_reduce<__bf16>;
+  }
+}
+
 LaunchFn scale_launcher(int c_dtype) {
   switch (c_dtype) {
     case 0: return &launch_scale<float>;

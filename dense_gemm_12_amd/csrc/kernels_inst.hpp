@@ -8,7 +8,7 @@ namespace mg {
 
 template <class Tile>
 hipError_t launch_tile(const GemmParams &p, hipStream_t s) {
-  hipLaunchKernelGGL(gemm_kernel<Tile>, dim3(p.tiles_m * p.tiles_n), dim3(Tile::NT), 0, s, p);
+  hipLaunchKernelGGL(gemm_kernel<Tile>, dim3(p.tiles_m * p.tiles_n * p.splits), dim3(Tile::NT), 0, s, p);
   return hipGetLastError();
 }
 
@@ -46,7 +46,8 @@ KernelEntry make_entry(const char *name) {
 
 template <class Tile>
 hipError_t launch_dma_tile(const GemmParams &p, hipStream_t s) {
-  hipLaunchKernelGGL(gemm_dma_kernel<Tile>, dim3(p.tiles_m * p.tiles_n), dim3(Tile::NT), 0, s, p);
+  hipLaunchKernelGGL(gemm_dma_kernel<Tile>, dim3(p.tiles_m * p.tiles_n * p.splits), dim3(Tile::NT), 0, s,
+                     p);
   return hipGetLastError();
 }
 

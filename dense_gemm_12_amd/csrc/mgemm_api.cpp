@@ -23,6 +23,8 @@ thread_local int g_last_hip_error = 0;
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;  // dimensions must be < 2^31
 constexpr int64_t kMaxLd = (int64_t)1 << 21;   // per-slice byte offsets stay below 2^31
+constexpr int kMaxSplits = 64;                  // split-K ranges per problem
+constexpr int64_t kFillWorkgroups = 256;        // one workgroup per CU
 
 int elem_size(int dtype) { return dtype == MG_F32 ? 4 : 2; }
 
@@ -198,10 +200,53 @@ Plan plan(const Problem &p) {
 
 }  // namespace
 
-// Implementation shared by the entry points.
-static mg_status run(const Problem &p, int forced, void *stream_v) {
+// Split-K shape: K cut into ranges of `chunk` (a multiple of bk) values;
+// returns the number of ranges, which may be below the requested s.
+int split_shape(int64_t K, int bk, int s, int *chunk) {
+  if (s <= 1 || K <= 0) {
+    *chunk = (int)K;
+    return 1;
+  }
+  const int64_t per = (K + s - 1) / s;
+  const int64_t c = (per + bk - 1) / bk * bk;
+  *chunk = (int)c;
+  return (int)((K + c - 1) / c);
+}
+
+// The planner's split count: 1 unless the tile grid leaves CUs idle; then
+// enough ranges to give every CU a workgroup, each at least two slices
+// deep, and no more than the workspace holds.
+int auto_splits(const Problem &p, const KernelEntry &k, int64_t ws_bytes) {
+  const int64_t t = tiles_for(p.M, p.N, k.bm, k.bn);
+  if (t >= kFillWorkgroups || p.K <= 0) return 1;
+  int64_t s = (kFillWorkgroups + t - 1) / t;
+  const int64_t by_k = p.K / (2 * (int64_t)k.bk);
+  const int64_t by_ws = ws_bytes / (p.M * p.N * 4);
+  if (s > by_k) s = by_k;
+  if (s > by_ws) s = by_ws;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return s < 2 ? 1 : (int)s;
+}
+
+// Implementation shared by the entry points.  splits: 0 = planner's choice
+// (bounded by the workspace), 1 = no split, >= 2 = that many K ranges.
+static mg_status run(const Problem &p, int forced, int splits, void *ws, size_t ws_bytes,
+                     void *stream_v) {
   mg_status s = validate(p);
   if (s != MG_OK) return s;
+  if (splits < 0 || splits > kMaxSplits) return MG_EINVAL;
+  if (ws_bytes > 0 && (ws == nullptr || (uintptr_t)ws % 16 != 0)) return MG_EINVAL;
+  if (splits > 1 && (int64_t)ws_bytes / splits < p.M * p.N * 4) return MG_EINVAL;
+  if (ws_bytes > 0 && p.M > 0 && p.N > 0) {
+    const int64_t wb = (int64_t)ws_bytes;
+    const int es = elem_size(p.in_type);
+    const int64_t a_rows = p.ta == MG_N ? p.M : p.K, a_cols = p.ta == MG_N ? p.K : p.M;
+    const int64_t b_rows = p.tb == MG_N ? p.K : p.N, b_cols = p.tb == MG_N ? p.N : p.K;
+    if (ranges_overlap(ws, wb, p.C, span_bytes(p.M, p.N, p.ldc, elem_size(p.c_type))) ||
+        ranges_overlap(ws, wb, p.A, span_bytes(a_rows, a_cols, p.lda, es)) ||
+        ranges_overlap(ws, wb, p.B, span_bytes(b_rows, b_cols, p.ldb, es)))
+      return MG_EINVAL;
+  }
   if (p.M == 0 || p.N == 0) return MG_OK;
   int n = 0;
   const KernelEntry *e = entries(p.in_type, &n);
@@ -220,6 +265,9 @@ static mg_status run(const Problem &p, int forced, void *stream_v) {
   gp.K = (int)p.K;
   gp.alpha = p.alpha;
   gp.beta = p.beta;
+  gp.splits = 1;
+  gp.k_chunk = (int)p.K;
+  gp.ws = nullptr;
   const int ces = elem_size(p.c_type);
   gp.c_vec = ((uintptr_t)p.C % (ces == 4 ? 16 : 8) == 0) && (p.ldc % 4 == 0);
   const int c_idx = p.c_type == MG_F32 ? 0 : (p.c_type == MG_F16 ? 1 : 2);
@@ -238,9 +286,17 @@ static mg_status run(const Problem &p, int forced, void *stream_v) {
     gp.tiles_m = (int)((p.M + k.bm - 1) / k.bm);
     gp.tiles_n = (int)((p.N + k.bn - 1) / k.bn);
     gp.group_m = 8;
+    int chunk = 0;
+    const int sp = split_shape(p.K, k.bk, splits == 0 ? auto_splits(p, k, (int64_t)ws_bytes) : splits,
+                               &chunk);
+    if ((int64_t)gp.tiles_m * gp.tiles_n * sp >= kMaxDim) return MG_EUNSUPPORTED;
+    gp.splits = sp;
+    gp.k_chunk = chunk;
+    gp.ws = static_cast<float *>(ws);
     const int c_is_f32 = (p.c_type == MG_F32) ? 1 : 0;
     const int a_kc = p.ta == MG_N ? 1 : 0, b_kc = p.tb == MG_T ? 1 : 0;
     err = k.fn[c_is_f32][a_kc][b_kc](gp, stream);
+    if (err == hipSuccess && sp > 1) err = mg::reduce_launcher(c_idx)(gp, stream);
   }
   if (err != hipSuccess) {
     g_last_hip_error = (int)err;
@@ -255,7 +311,7 @@ mg_status gemm_f32_cfg(int config, mg_op ta, mg_op tb, int64_t M, int64_t N, int
                        float alpha, const float *A, int64_t lda, const float *B, int64_t ldb,
                        float beta, float *C, int64_t ldc, void *stream) {
   Problem p{MG_F32, MG_F32, (int)ta, (int)tb, M, N, K, lda, ldb, ldc, alpha, beta, A, B, C};
-  return run(p, config, stream);
+  return run(p, config, 1, nullptr, 0, stream);
 }
 
 mg_status gemm_f16_cfg(int config, mg_op ta, mg_op tb, int64_t M, int64_t N, int64_t K,
@@ -263,7 +319,7 @@ mg_status gemm_f16_cfg(int config, mg_op ta, mg_op tb, int64_t M, int64_t N, int
                        int64_t ldb, float beta, void *C, mg_dtype c_type, int64_t ldc,
                        void *stream) {
   Problem p{MG_F16, (int)c_type, (int)ta, (int)tb, M, N, K, lda, ldb, ldc, alpha, beta, A, B, C};
-  return run(p, config, stream);
+  return run(p, config, 1, nullptr, 0, stream);
 }
 
 mg_status gemm_bf16_cfg(int config, mg_op ta, mg_op tb, int64_t M, int64_t N, int64_t K,
@@ -271,7 +327,7 @@ mg_status gemm_bf16_cfg(int config, mg_op ta, mg_op tb, int64_t M, int64_t N, in
                         int64_t ldb, float beta, void *C, mg_dtype c_type, int64_t ldc,
                         void *stream) {
   Problem p{MG_BF16, (int)c_type, (int)ta, (int)tb, M, N, K, lda, ldb, ldc, alpha, beta, A, B, C};
-  return run(p, config, stream);
+  return run(p, config, 1, nullptr, 0, stream);
 }
 
 mg_status gemm_f32(mg_op ta, mg_op tb, int64_t M, int64_t N, int64_t K, float alpha,
@@ -290,6 +346,31 @@ mg_status gemm_bf16(mg_op ta, mg_op tb, int64_t M, int64_t N, int64_t K, float a
                     const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, float beta,
                     void *C, mg_dtype c_type, int64_t ldc, void *stream) {
   return gemm_bf16_cfg(-1, ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream);
+}
+
+mg_status gemm_ex(mg_dtype in_type, mg_dtype c_type, mg_op ta, mg_op tb, int64_t M, int64_t N,
+                  int64_t K, float alpha, const void *A, int64_t lda, const void *B, int64_t ldb,
+                  float beta, void *C, int64_t ldc, void *workspace, size_t workspace_bytes,
+                  int config, int splits, void *stream) {
+  if ((int)in_type < MG_F32 || (int)in_type > MG_BF16) return MG_EINVAL;
+  Problem p{(int)in_type, (int)c_type, (int)ta, (int)tb, M, N, K, lda, ldb, ldc, alpha, beta, A, B, C};
+  return run(p, config, splits, workspace, workspace_bytes, stream);
+}
+
+size_t mg_workspace_size(mg_dtype in_type, mg_dtype c_type, mg_op ta, mg_op tb, int64_t M, int64_t N,
+                         int64_t K, int64_t lda, int64_t ldb) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  if ((int)in_type < MG_F32 || (int)in_type > MG_BF16) return 0;
+  // Planned as for 16-byte-aligned base pointers with the given leading dimensions.
+  Problem p{(int)in_type, (int)c_type, (int)ta, (int)tb, M, N, K, lda, ldb, N, 1.0f, 0.0f,
+            (const void *)(uintptr_t)4096, (const void *)(uintptr_t)4096, nullptr};
+  const int cfg = plan(p).config;
+  if (cfg < 0) return 0;
+  int n = 0;
+  const KernelEntry &k = entries(p.in_type, &n)[cfg];
+  int chunk = 0;
+  const int sp = split_shape(K, k.bk, auto_splits(p, k, INT64_MAX), &chunk);
+  return sp > 1 ? (size_t)sp * (size_t)M * (size_t)N * 4 : 0;
 }
 
 int mg_num_configs(mg_dtype in_type) {

@@ -49,6 +49,7 @@
 #ifndef MGEMM_H
 #define MGEMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -92,6 +93,47 @@ mg_status gemm_bf16_cfg(int config, mg_op ta, mg_op tb, int64_t M, int64_t N, in
                         float alpha, const uint16_t *A, int64_t lda, const uint16_t *B,
                         int64_t ldb, float beta, void *C, mg_dtype c_type, int64_t ldc,
                         void *stream);
+
+/* Split-K GEMM with a caller-provided workspace: any of the three operations
+ * (in_type MG_F32 with c_type MG_F32; MG_F16 or MG_BF16 with their own type or
+ * MG_F32 as c_type), with A, B, C and the arguments as above.
+ *
+ * The K dimension is cut into `splits` contiguous ranges.  Each range's
+ * partial product is written in fp32 to `workspace`; a second kernel, on the
+ * same stream, sums the partials in range order and applies alpha and beta
+ * with one rounding to the C type.  This is the split of "如何优化一个 CUDA
+ * Matmul Kernel" (the worklog), section Kernel 10: Warptiling (its look at the
+ * kernels cuBLAS picks for small shapes: a matmul kernel followed by a
+ * reduction kernel over extra memory), also named in "SGEMM CUDA代码学习",
+ * 第6步 (cuBLAS gap review).  It fills the GPU when M x N gives few tiles and K
+ * is long.  Results are deterministic (identical bits on every run with the
+ * same arguments) and within the same error bound as the unsplit call, whose
+ * last bits they may not match.
+ *
+ *   splits     0: the planner's choice: a single range (the plain kernel)
+ *                 when the tiles already fill the GPU, else enough ranges to
+ *                 give every CU work, each at least two K slices deep, and no
+ *                 more than workspace_bytes holds; 1: no split; 2..64: at most
+ *                 that many ranges (the ranges are whole K slices, so fewer
+ *                 may result).
+ *   workspace  device memory owned by the caller, 16-byte aligned, not
+ *              overlapping A, B or C, of at least splits * M * N * 4 bytes
+ *              when splits >= 2 (see mg_workspace_size); may be NULL when
+ *              workspace_bytes is 0.  Its contents on entry are ignored; it
+ *              is scratch until the call's kernels have finished.
+ *   config     as for the _cfg entry points (-1: the planner's choice).
+ * Errors: as above, plus MG_EINVAL for splits outside 0..64, a misaligned or
+ * overlapping workspace, or one smaller than a forced split count needs. */
+mg_status gemm_ex(mg_dtype in_type, mg_dtype c_type, mg_op ta, mg_op tb, int64_t M, int64_t N,
+                  int64_t K, float alpha, const void *A, int64_t lda, const void *B, int64_t ldb,
+                  float beta, void *C, int64_t ldc, void *workspace, size_t workspace_bytes,
+                  int config, int splits, void *stream);
+
+/* Workspace bytes that gemm_ex with splits = 0 uses for this problem when
+ * given enough (0 when it would not split), for 16-byte-aligned base
+ * pointers with these leading dimensions. */
+size_t mg_workspace_size(mg_dtype in_type, mg_dtype c_type, mg_op ta, mg_op tb, int64_t M, int64_t N,
+                         int64_t K, int64_t lda, int64_t ldb);
 
 /* Kernel configurations available for an input type, and their names
  * (static strings, e.g. "mfma_256x256x64_w2x2"). */

@@ -31,12 +31,18 @@ def stored_shapes(M, N, K, ta, tb):
     return ((K, M) if ta else (M, K)), ((N, K) if tb else (K, N))
 
 
+GUARD = 256  # bytes after a split-K workspace that the library must not touch
+
+
 def run_gpu(A, B, Cin, *, alpha, beta, ta, tb, c_dtype, config=-1, ldc=None, stream=None,
-            offset_elems=0):
+            offset_elems=0, workspace_bytes=None, splits=0):
     """Copy host tensors to the GPU, run the library's GEMM, return C on the host.
 
     ``ldc`` > N places C inside a wider buffer; ``offset_elems`` shifts every
-    operand's base address by that many elements (misalignment tests)."""
+    operand's base address by that many elements (misalignment tests).
+    ``workspace_bytes`` (with ``splits``) runs the split-K entry point with a
+    workspace of that size, pre-filled with 0xff bytes (NaN as fp32) and
+    followed by GUARD bytes that must come back untouched."""
     import dense_gemm_12_amd as mg
     dev = torch.device("cuda:0")
 
@@ -67,9 +73,16 @@ def run_gpu(A, B, Cin, *, alpha, beta, ta, tb, c_dtype, config=-1, ldc=None, str
         Cd = up(Cin_t)
     if stream is not None:
         stream.wait_stream(torch.cuda.current_stream())  # uploads ran on the current stream
+    ws = None
+    if workspace_bytes is not None:
+        ws_all = torch.full((workspace_bytes + GUARD,), 0xFF, dtype=torch.uint8, device=dev)
+        ws_all[workspace_bytes:] = 0xAB
+        ws = ws_all[:workspace_bytes]
     mg.gemm(Ad, Bd, Cd, alpha=alpha, beta=beta, trans_a=ta, trans_b=tb, config=config,
-            stream=stream)
+            stream=stream, workspace=ws, splits=splits)
     torch.cuda.synchronize()
+    if ws is not None:
+        assert torch.all(ws_all[workspace_bytes:] == 0xAB).item(), "GEMM wrote past its workspace"
     if Cbig is not None:
         assert torch.all(Cbig[:, N:].float() == 7.0).item(), "GEMM wrote outside C's columns"
     return Cd.cpu()

@@ -170,3 +170,39 @@ def test_product_path_has_no_oracle_or_cpu_fallback():
             "try:\n    mg.load('/nonexistent/libmgemm.so')\nexcept RuntimeError:\n    print('raised')\n")
     out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
     assert "raised" in out.stdout
+
+
+def ex(mg, M=64, N=64, K=256, ws=1 << 30, ws_bytes=1 << 20, splits=0, A=FAKE_A, B=FAKE_B, C=FAKE_C,
+       in_type=0, c_type=0):
+    return mg.load().gemm_ex(in_type, c_type, 0, 0, M, N, K, 1.0, A, K, B, N, 0.0, C, N, ws, ws_bytes,
+                             -1, splits, None)
+
+
+def test_split_k_arguments_are_rejected_before_launch(mg):
+    E = mg.MG_EINVAL
+    assert ex(mg, splits=-1) == E
+    assert ex(mg, splits=65) == E
+    assert ex(mg, ws=None, ws_bytes=16) == E            # NULL workspace with a size
+    assert ex(mg, ws=(1 << 30) + 8) == E                # not 16-byte aligned
+    assert ex(mg, splits=4, ws_bytes=4 * 64 * 64 * 4 - 16) == E  # too small for a forced split
+    assert ex(mg, ws=FAKE_C + 64) == E                  # overlaps C
+    assert ex(mg, ws=FAKE_A - 64, ws_bytes=4096) == E   # overlaps A
+    assert ex(mg, in_type=7) == E
+    assert ex(mg, in_type=1, c_type=0, M=-1) == E
+    # empty problems finish on the host, whatever the workspace
+    assert ex(mg, M=0, splits=8, ws_bytes=0) == mg.MG_OK  # 8 empty partials need no bytes
+    assert ex(mg, M=0, splits=0) == mg.MG_OK
+    assert ex(mg, M=0, ws=None, ws_bytes=0) == mg.MG_OK
+
+
+def test_workspace_size_matches_the_split_rule(mg):
+    """The planner splits only when the tile grid leaves CUs idle: the odd-K
+    bf16 problem (one 128-row tile row of 32 tiles) takes 8 ranges of 512;
+    a 4096^3 problem never splits."""
+    lib = mg.load()
+    w = lib.mg_workspace_size(mg.MG_BF16, mg.MG_F32, 0, 0, 127, 4096, 4095, 4095, 4096)
+    assert w == 8 * 127 * 4096 * 4
+    assert lib.mg_workspace_size(mg.MG_F16, mg.MG_F16, 0, 1, 4096, 4096, 4096, 4096, 4096) == 0
+    assert lib.mg_workspace_size(mg.MG_F32, mg.MG_F32, 0, 0, 0, 4096, 4096, 4096, 4096) == 0
+    # short K: no split (each range must be at least two K slices)
+    assert lib.mg_workspace_size(mg.MG_F32, mg.MG_F32, 0, 0, 64, 64, 64, 64, 64) == 0
