@@ -15,12 +15,21 @@ fraction of MI355X's dense peak for its dtype, the roofline of the dominant
 kernel (its average launch time from HIP events recorded on the launch
 stream) and the CPU oracle timed on a bounded sample of the same step.
 
+After the timed steps (outside the timed region): each part is timed again
+with cold caches (a 512 MiB write before every launch, events around the
+GEMM alone); the GPU clocks and power are read with rocm-smi while untimed
+steps run; and a cache-blocked CPU GEMM (cpu_gemm/, fp32 accumulation, all
+cores) runs the whole step as a second CPU baseline.  A workload whose tile
+grid leaves CUs idle runs through the split-K entry point with the
+workspace the planner asks for.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-                       [--workload NAME ...]
+                       [--cold-steps N] [--no-clocks] [--workload NAME ...]
 """
 from __future__ import annotations
 
 import argparse
+import subprocess
 import json
 import os
 import platform
@@ -115,6 +124,49 @@ def cpu_baseline(parts, target_s):
             "seconds": round(total_s, 2), "cpu": platform.processor() or platform.machine()}
 
 
+def cpu_blocked(parts):
+    """The blocked CPU GEMM (cpu_gemm/, fp32 accumulation, all cores) on every
+    part of the step, whole problems."""
+    import cpu_gemm
+    threads = len(os.sched_getaffinity(0))
+    cpu_gemm.load()
+    total_flops, total_s, desc = 0.0, 0.0, []
+    for name, (A, B, C) in parts:
+        w = gi.WORKLOADS[name]
+        An, Bn = gi.as_numpy_bits(A), gi.as_numpy_bits(B)
+        Cn = None if C is None else C.float().numpy()
+        t0 = time.perf_counter()
+        cpu_gemm.gemm_rows(An, Bn, in_dtype=w["in_dtype"], ta=w["ta"], tb=w["tb"], M=w["M"], N=w["N"],
+                           K=w["K"], alpha=w["alpha"], beta=w["beta"], Cin=Cn, threads=threads)
+        dt = time.perf_counter() - t0
+        total_flops += flops(w)
+        total_s += dt
+        desc.append(f"{name}: whole problem, {dt:.2f} s")
+    return {"value": total_flops / total_s / 1e12, "unit": "TFLOPS", "cores": threads,
+            "kind": "blocked", "sample": "; ".join(desc) + "; cache-blocked, packed, fp32 accumulate, "
+            "gcc -O3 -march=native, threads over column stripes", "seconds": round(total_s, 2),
+            "cpu": cpu_gemm.cpu_model()}
+
+
+def read_clocks():
+    """GPU clocks and power from rocm-smi (None where it cannot say)."""
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        data = json.loads(r.stdout)
+    except Exception:
+        return None
+    card = next((v for k, v in data.items() if k.startswith("card")), None)
+    if not isinstance(card, dict):
+        return None
+    out = {}
+    for k, v in card.items():
+        key = k.lower()
+        if key.startswith(("sclk", "mclk", "fclk", "socclk")) or "power" in key:
+            out[k] = v
+    return out or None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -124,6 +176,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--workload", nargs="*", default=None,
                     help=f"named workloads instead of the metric's step {STEP}")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="extra steps with a 512 MiB cache scrub before each launch (0: skip)")
+    ap.add_argument("--no-clocks", action="store_true", help="skip the rocm-smi clock reading")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -148,16 +203,24 @@ def main():
         Cd = (C.to(dev) if C is not None else
               torch.empty((w["M"], w["N"]), dtype=gi.DTYPES[w["c_dtype"]], device=dev))
         parts_dev.append((Ad, Bd, Cd))
-        calls.append((name, w, Ad, Bd, Cd))
+        # problems whose tile grid leaves CUs idle run split-K with a workspace
+        codes = mg.DTYPE_CODES
+        wsb = mg.workspace_size(codes[w["in_dtype"]], codes[w["c_dtype"]], int(w["ta"]), int(w["tb"]),
+                                w["M"], w["N"], w["K"], Ad.stride(0), Bd.stride(0))
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+        calls.append((name, w, Ad, Bd, Cd, ws))
 
     stream = torch.cuda.current_stream(dev)
 
+    def launch(w, Ad, Bd, Cd, ws):
+        mg.gemm(Ad, Bd, Cd, alpha=w["alpha"], beta=w["beta"], trans_a=w["ta"], trans_b=w["tb"],
+                stream=stream, workspace=ws)
+
     def step(evs=None):
-        for i, (name, w, Ad, Bd, Cd) in enumerate(calls):
+        for i, (name, w, Ad, Bd, Cd, ws) in enumerate(calls):
             if evs is not None:
                 evs[i][0].record(stream)
-            mg.gemm(Ad, Bd, Cd, alpha=w["alpha"], beta=w["beta"], trans_a=w["ta"],
-                    trans_b=w["tb"], stream=stream)
+            launch(w, Ad, Bd, Cd, ws)
             if evs is not None:
                 evs[i][1].record(stream)
 
@@ -174,6 +237,39 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
+    cold_ms = None
+    if args.cold_steps > 0:
+        # Cold caches: a 512 MiB write (twice the Infinity Cache) before every
+        # launch evicts A, B and C; the events bracket the GEMM alone.
+        scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in calls]
+               for _ in range(args.cold_steps)]
+        log(f"timing {args.cold_steps} cold-cache steps")
+        for k in range(args.cold_steps):
+            for i, (name, w, Ad, Bd, Cd, ws) in enumerate(calls):
+                scrub.fill_(k & 0xff)
+                cev[k][i][0].record(stream)
+                launch(w, Ad, Bd, Cd, ws)
+                cev[k][i][1].record(stream)
+        torch.cuda.synchronize()
+        cold_ms = [sum(cev[k][i][0].elapsed_time(cev[k][i][1]) for k in range(args.cold_steps)) /
+                   args.cold_steps for i in range(len(calls))]
+        del scrub
+    clocks = None
+    if not args.no_clocks:
+        # clocks under the same load, read while an untimed copy of the step runs
+        import threading
+        box = {}
+        th = threading.Thread(target=lambda: box.setdefault("c", read_clocks()))
+        th.start()
+        t_end = time.perf_counter() + 30.0
+        while th.is_alive() and time.perf_counter() < t_end:
+            for _ in range(5):
+                step()
+            torch.cuda.synchronize()
+        th.join()
+        clocks = box.get("c")
+
     step_flops = sum(flops(w) for _, w, *_ in calls)
     value = args.steps * step_flops / elapsed / 1e12
     parts = []
@@ -187,7 +283,12 @@ def main():
                       "peak_tflops": PEAK_TFLOPS[w["in_dtype"]],
                       "frac_of_peak": round(tf / PEAK_TFLOPS[w["in_dtype"]], 4),
                       "min_hbm_bytes": min_bytes(w),
+                      "split_k_workspace_bytes": 0 if calls[i][5] is None else calls[i][5].numel(),
                       "pages_context": PAGES_CONTEXT.get(name)})
+        if cold_ms is not None:
+            parts[-1]["us_per_launch_cold"] = round(cold_ms[i] * 1e3, 2)
+            parts[-1]["tflops_cold"] = round(flops(w) / (cold_ms[i] * 1e-3) / 1e12, 2)
+            parts[-1]["hbm_gbps_cold_min_bytes"] = round(min_bytes(w) / (cold_ms[i] * 1e-3) / 1e9, 1)
     dom = max(range(len(parts)), key=lambda i: parts[i]["us_per_launch"])
     d, dw = parts[dom], calls[dom][1]
     traffic = load_traffic(d["kernel"], d["workload"])
@@ -203,11 +304,13 @@ def main():
         "dtype": "+".join(sorted({w["in_dtype"] for _, w, *_ in calls})),
         "data": "synthetic: seeded fp32 N(0,1) and fp16 N(0,1)/sqrt(K) matrices, resident in HBM",
         "config": {"workload": " + ".join(names), "parts": list(names)},
-        "parts": parts, "roofline": roofline,
+        "parts": parts, "roofline": roofline, "gpu_clocks_under_load": clocks,
     }
     if not args.no_cpu and rank == 0:
         log("CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline(parts_host, args.cpu_seconds)
+        log("CPU blocked baseline")
+        out["cpu_blocked"] = cpu_blocked(parts_host)
     if rank == 0:
         print(json.dumps(out), flush=True)
 

@@ -27,6 +27,15 @@ COMMON = [
 ]
 
 
+# Per-source flags.  fp32 tiles: keep MFMA accumulators in VGPRs.  In the
+# AGPR form the register allocator gives the last MFMA of each accumulator
+# chain a fresh AGPR tuple and rotates all of them back at the loop edge
+# (hundreds of v_accvgpr moves per K slice); every fp32 tile fits in VGPRs at
+# its occupancy.  The 16-bit tiles with 256 accumulators per lane need AGPRs,
+# so the flag is not global.
+FILE_FLAGS = {"kernels_f32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith((".hip", ".cpp")))
@@ -34,7 +43,7 @@ def sources():
 
 def _compile(src: str, extra: list[str]) -> str:
     obj = os.path.join(OUT_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, *extra, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
