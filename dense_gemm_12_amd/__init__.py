@@ -26,7 +26,7 @@ DTYPE_CODES = {"f32": MG_F32, "f16": MG_F16, "bf16": MG_BF16}
 # Every exported symbol of include/mgemm.h.
 EXPORTS = (
     "gemm_f32", "gemm_f16", "gemm_bf16", "gemm_f32_cfg", "gemm_f16_cfg", "gemm_bf16_cfg",
-    "gemm_ex", "mg_workspace_size", "mg_num_configs", "mg_config_name", "mg_chosen_config", "mg_load_tune_table",
+    "gemm_ex", "mg_workspace_size", "gemm_f32_split16", "mg_split16_workspace_size", "mg_num_configs", "mg_config_name", "mg_chosen_config", "mg_load_tune_table",
     "mg_tune_table_size", "mg_status_str", "mg_last_hip_error", "mg_version",
 )
 
@@ -70,6 +70,11 @@ def load(path: str | None = None):
         lib.gemm_ex.restype = ci
         lib.mg_workspace_size.argtypes = [ci, ci, ci, ci, i64, i64, i64, i64, i64]
         lib.mg_workspace_size.restype = ctypes.c_size_t
+        lib.gemm_f32_split16.argtypes = [ci, ci, i64, i64, i64, f, vp, i64, vp, i64, f, vp, i64, vp,
+                                         ctypes.c_size_t, vp]
+        lib.gemm_f32_split16.restype = ci
+        lib.mg_split16_workspace_size.argtypes = [i64, i64, i64]
+        lib.mg_split16_workspace_size.restype = ctypes.c_size_t
         lib.mg_num_configs.argtypes = [ci]
         lib.mg_num_configs.restype = ci
         lib.mg_config_name.argtypes = [ci, ci]
@@ -141,6 +146,16 @@ def workspace_size(in_type, c_type, ta, tb, M, N, K, lda, ldb) -> int:
     return load().mg_workspace_size(in_type, c_type, ta, tb, M, N, K, lda, ldb)
 
 
+def gemm_f32_split16(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspace_bytes,
+                     stream=None):
+    _check(load().gemm_f32_split16(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+                                   workspace_bytes, stream), "gemm_f32_split16")
+
+
+def split16_workspace_size(M, N, K) -> int:
+    return load().mg_split16_workspace_size(M, N, K)
+
+
 def num_configs(in_type: str) -> int:
     return load().mg_num_configs(DTYPE_CODES[in_type])
 
@@ -176,7 +191,8 @@ def _ld(t) -> int:
 
 
 def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, trans_a: bool = False,
-         trans_b: bool = False, config: int = -1, stream=None, workspace=None, splits: int = 0):
+         trans_b: bool = False, config: int = -1, stream=None, workspace=None, splits: int = 0,
+         split16: bool = False):
     """C <- alpha * op(A) @ op(B) + beta * C on C's device, in place.
 
     A, B, C are 2-D CUDA tensors holding the *stored* matrices (A is K x M when
@@ -187,6 +203,10 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, trans_a: bool = False,
     With ``workspace`` (a CUDA tensor used as raw bytes, see
     ``workspace_size``) the call goes through ``gemm_ex`` and may split K
     (``splits``: 0 = the planner's choice, 1 = never, n = that many ranges).
+
+    ``split16`` (fp32 only) runs ``gemm_f32_split16``: fp32 through the fp16
+    matrix cores; ``workspace`` must then hold ``split16_workspace_size``
+    bytes (a buffer of that size is taken from torch's allocator if None).
     """
     import torch
     if A.dtype != B.dtype:
@@ -200,6 +220,15 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, trans_a: bool = False,
     s = (stream or torch.cuda.current_stream(C.device)).cuda_stream
     ta, tb = (MG_T if trans_a else MG_N), (MG_T if trans_b else MG_N)
     args = (M, N, K, float(alpha), A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), float(beta))
+    if split16:
+        if A.dtype != torch.float32 or C.dtype != torch.float32:
+            raise TypeError("split16 computes fp32 GEMMs")
+        need = split16_workspace_size(M, N, K)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=C.device)
+        gemm_f32_split16(ta, tb, *args, C.data_ptr(), _ld(C), workspace.data_ptr(),
+                         workspace.numel() * workspace.element_size(), s)
+        return C
     if workspace is not None or splits not in (0, 1):
         codes = {torch.float32: MG_F32, torch.float16: MG_F16, torch.bfloat16: MG_BF16}
         if A.dtype not in codes or C.dtype not in codes:

@@ -20,6 +20,8 @@ __device__ __forceinline__ GemmParams partial_params(const GemmParams &p, int kb
   q.alpha = 1.0f;
   q.beta = 0.0f;
   q.c_vec = (p.N % 4) == 0;
+  q.row_exp = nullptr;  // partials are raw sums; the reduction unscales
+  q.col_exp = nullptr;
   return q;
 }
 
@@ -84,10 +86,19 @@ struct GemmEpilogue {
     }
   }
 
+  // x[e] *= 2^-(row_exp[m] + col_exp[n + e]) (exact unless the result leaves
+  // fp32's range); masked tail columns read a valid exponent and are dropped.
+  static __device__ __forceinline__ void unscale(const GemmParams &p, int m, int n, float (&x)[4]) {
+    const int re = p.row_exp[m];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = ldexpf(x[e], -(re + p.col_exp[min(n + e, p.N - 1)]));
+  }
+
   static __device__ __forceinline__ void store(const GemmParams &p, const f32x4 (&acc)[MI][NJ],
                                                int mw, int nw, int lane) {
     TO *C = static_cast<TO *>(p.C);
     const bool use_beta = p.beta != 0.0f;
+    const bool scaled = p.row_exp != nullptr;
     const int r = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
@@ -99,7 +110,8 @@ struct GemmEpilogue {
         for (int j = 0; j < NJ; ++j) {
           const int n = nw + j * 16 + g * 4;
           if (n >= p.N) continue;
-          const float x[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+          float x[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+          if (scaled) unscale(p, m, n, x);
           store4(p, crow, n, x, use_beta);
         }
       } else {
@@ -109,8 +121,9 @@ struct GemmEpilogue {
           for (int v = 0; v < 4; ++v) {
             const int n = nw + 64 * q + 16 * g + 4 * v;
             if (n >= p.N) continue;
-            const float x[4] = {acc[i][4 * q][v], acc[i][4 * q + 1][v], acc[i][4 * q + 2][v],
-                                acc[i][4 * q + 3][v]};
+            float x[4] = {acc[i][4 * q][v], acc[i][4 * q + 1][v], acc[i][4 * q + 2][v],
+                          acc[i][4 * q + 3][v]};
+            if (scaled) unscale(p, m, n, x);
             store4(p, crow, n, x, use_beta);
           }
       }

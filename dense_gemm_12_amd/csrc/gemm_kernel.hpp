@@ -326,6 +326,7 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmParams p) {
         for (int e = 0; e < 4; ++e)
           if (n + e < p.N) x[e] += w[s * slab + e];
     }
+    if (p.row_exp != nullptr) GemmEpilogue<TO, 1, 1>::unscale(p, m, n, x);
     GemmEpilogue<TO, 1, 1>::store4(p, static_cast<TO *>(p.C) + (int64_t)m * p.ldc, n, x, use_beta);
   }
 }

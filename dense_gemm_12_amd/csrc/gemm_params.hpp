@@ -24,6 +24,11 @@ struct GemmParams {
   int splits;
   int k_chunk;            // multiple of every tile's BK
   float *ws;
+  // Power-of-two unscaling of the product (fp32 through split fp16 inputs):
+  // when row_exp is non-null, element (m, n) of the product is multiplied by
+  // 2^-(row_exp[m] + col_exp[n]) before alpha and beta are applied.
+  const int *row_exp;
+  const int *col_exp;
 };
 
 typedef hipError_t (*LaunchFn)(const GemmParams &, hipStream_t);

@@ -13,6 +13,7 @@
 
 #include "../../include/mgemm.h"
 #include "gemm_params.hpp"
+#include "split16.hpp"
 
 using mg::GemmParams;
 using mg::KernelEntry;
@@ -202,7 +203,7 @@ Plan plan(const Problem &p) {
 
 // Split-K shape: K cut into ranges of `chunk` (a multiple of bk) values;
 // returns the number of ranges, which may be below the requested s.
-int split_shape(int64_t K, int bk, int s, int *chunk) {
+static int split_shape(int64_t K, int bk, int s, int *chunk) {
   if (s <= 1 || K <= 0) {
     *chunk = (int)K;
     return 1;
@@ -216,7 +217,7 @@ int split_shape(int64_t K, int bk, int s, int *chunk) {
 // The planner's split count: 1 unless the tile grid leaves CUs idle; then
 // enough ranges to give every CU a workgroup, each at least two slices
 // deep, and no more than the workspace holds.
-int auto_splits(const Problem &p, const KernelEntry &k, int64_t ws_bytes) {
+static int auto_splits(const Problem &p, const KernelEntry &k, int64_t ws_bytes) {
   const int64_t t = tiles_for(p.M, p.N, k.bm, k.bn);
   if (t >= kFillWorkgroups || p.K <= 0) return 1;
   int64_t s = (kFillWorkgroups + t - 1) / t;
@@ -231,7 +232,7 @@ int auto_splits(const Problem &p, const KernelEntry &k, int64_t ws_bytes) {
 // Implementation shared by the entry points.  splits: 0 = planner's choice
 // (bounded by the workspace), 1 = no split, >= 2 = that many K ranges.
 static mg_status run(const Problem &p, int forced, int splits, void *ws, size_t ws_bytes,
-                     void *stream_v) {
+                     void *stream_v, const int *row_exp = nullptr, const int *col_exp = nullptr) {
   mg_status s = validate(p);
   if (s != MG_OK) return s;
   if (splits < 0 || splits > kMaxSplits) return MG_EINVAL;
@@ -268,6 +269,8 @@ static mg_status run(const Problem &p, int forced, int splits, void *ws, size_t 
   gp.splits = 1;
   gp.k_chunk = (int)p.K;
   gp.ws = nullptr;
+  gp.row_exp = row_exp;
+  gp.col_exp = col_exp;
   const int ces = elem_size(p.c_type);
   gp.c_vec = ((uintptr_t)p.C % (ces == 4 ? 16 : 8) == 0) && (p.ldc % 4 == 0);
   const int c_idx = p.c_type == MG_F32 ? 0 : (p.c_type == MG_F16 ? 1 : 2);
@@ -305,7 +308,90 @@ static mg_status run(const Problem &p, int forced, int splits, void *ws, size_t 
   return MG_OK;
 }
 
+// ---------------------------------------------- fp32 through split fp16 --
+static constexpr int64_t kSplit16Max = (int64_t)1 << 22;  // grid-dimension limits of the split kernels
+
+struct Split16Layout {
+  int64_t Kp;
+  int parts;
+  size_t a, b, re, ce, pm, total;  // byte offsets of the workspace sections
+};
+
+static Split16Layout split16_layout(int64_t M, int64_t N, int64_t K) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  Split16Layout L{};
+  L.Kp = (K + 63) / 64 * 64;
+  L.parts = (int)(K / 256 < 1 ? 1 : (K / 256 > 16 ? 16 : K / 256));
+  L.a = 0;
+  L.b = L.a + up((size_t)M * 3 * L.Kp * 2);
+  L.re = L.b + up((size_t)N * 3 * L.Kp * 2);
+  L.ce = L.re + up((size_t)M * 4);
+  L.pm = L.ce + up((size_t)N * 4);
+  L.total = L.pm + up((size_t)L.parts * (M > N ? M : N) * 4);
+  return L;
+}
+
+static mg_status split16_run(const Problem &p, void *ws, size_t ws_bytes, void *stream_v) {
+  mg_status s = validate(p);
+  if (s != MG_OK) return s;
+  if (p.M == 0 || p.N == 0) return MG_OK;
+  if (p.K == 0 || p.alpha == 0.0f) return run(p, -1, 1, nullptr, 0, stream_v);  // C = beta * C
+  if (p.M > kSplit16Max || p.N > kSplit16Max || p.K > kSplit16Max) return MG_EUNSUPPORTED;
+  const Split16Layout L = split16_layout(p.M, p.N, p.K);
+  if (3 * L.Kp > kMaxLd) return MG_EUNSUPPORTED;
+  if (ws == nullptr || (uintptr_t)ws % 16 != 0 || ws_bytes < L.total) return MG_EINVAL;
+  {
+    const int64_t wb = (int64_t)ws_bytes;
+    const int64_t a_rows = p.ta == MG_N ? p.M : p.K, a_cols = p.ta == MG_N ? p.K : p.M;
+    const int64_t b_rows = p.tb == MG_N ? p.K : p.N, b_cols = p.tb == MG_N ? p.N : p.K;
+    if (ranges_overlap(ws, wb, p.C, span_bytes(p.M, p.N, p.ldc, 4)) ||
+        ranges_overlap(ws, wb, p.A, span_bytes(a_rows, a_cols, p.lda, 4)) ||
+        ranges_overlap(ws, wb, p.B, span_bytes(b_rows, b_cols, p.ldb, 4)))
+      return MG_EINVAL;
+  }
+  char *w = static_cast<char *>(ws);
+  mg::Split16Plan sp{};
+  sp.A = static_cast<const float *>(p.A);
+  sp.B = static_cast<const float *>(p.B);
+  sp.lda = p.lda;
+  sp.ldb = p.ldb;
+  sp.M = (int)p.M;
+  sp.N = (int)p.N;
+  sp.K = (int)p.K;
+  sp.Kp = (int)L.Kp;
+  sp.a_rows_contiguous = p.ta == MG_N;
+  sp.b_cols_contiguous = p.tb == MG_T;
+  sp.parts = L.parts;
+  sp.Ap = reinterpret_cast<uint16_t *>(w + L.a);
+  sp.Bp = reinterpret_cast<uint16_t *>(w + L.b);
+  sp.row_exp = reinterpret_cast<int *>(w + L.re);
+  sp.col_exp = reinterpret_cast<int *>(w + L.ce);
+  sp.pmax = reinterpret_cast<float *>(w + L.pm);
+  hipError_t err = mg::split16_prepare(sp, static_cast<hipStream_t>(stream_v));
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    return MG_EHIP;
+  }
+  // A' B'^T over K' = 3 Kp: the TN fp16 GEMM with fp32 C and the unscaling.
+  const int64_t kq = 3 * L.Kp;
+  Problem q{MG_F16, MG_F32, MG_N, MG_T, p.M, p.N, kq, kq, kq, p.ldc, p.alpha, p.beta, sp.Ap, sp.Bp, p.C};
+  return run(q, -1, 1, nullptr, 0, stream_v, sp.row_exp, sp.col_exp);
+}
+
 extern "C" {
+
+mg_status gemm_f32_split16(mg_op ta, mg_op tb, int64_t M, int64_t N, int64_t K, float alpha,
+                           const float *A, int64_t lda, const float *B, int64_t ldb, float beta,
+                           float *C, int64_t ldc, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+  Problem p{MG_F32, MG_F32, (int)ta, (int)tb, M, N, K, lda, ldb, ldc, alpha, beta, A, B, C};
+  return split16_run(p, workspace, workspace_bytes, stream);
+}
+
+size_t mg_split16_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return split16_layout(M, N, K).total;
+}
 
 mg_status gemm_f32_cfg(int config, mg_op ta, mg_op tb, int64_t M, int64_t N, int64_t K,
                        float alpha, const float *A, int64_t lda, const float *B, int64_t ldb,

@@ -135,6 +135,39 @@ mg_status gemm_ex(mg_dtype in_type, mg_dtype c_type, mg_op ta, mg_op tb, int64_t
 size_t mg_workspace_size(mg_dtype in_type, mg_dtype c_type, mg_op ta, mg_op tb, int64_t M, int64_t N,
                          int64_t K, int64_t lda, int64_t ldb);
 
+/* fp32 GEMM through the fp16 matrix cores (C = alpha * op(A) * op(B) + beta * C,
+ * fp32 A, B, C, arguments and special cases as for gemm_f32), for callers
+ * who want fp32 results faster than the fp32 MFMA peak allows.
+ *
+ * "SGEMM CUDA代码学习", 第5步, trades accuracy for speed by rounding fp32 inputs
+ * to TF32 for the tensor cores.  This entry keeps fp32-level accuracy
+ * instead: each row of op(A) and column of op(B) is scaled by a power of two
+ * that brings its largest magnitude into [2^14, 2^15), every scaled value v
+ * is split into hi = fp16(v) and lo = fp16(v - hi), and
+ *   op(A) op(B) ~ A_hi B_hi + A_hi B_lo + A_lo B_hi
+ * runs as one fp16 GEMM with fp32 accumulation over 3 K (the split of
+ * Markidis et al., 2018, with the scaling of Ootomo and Yokota, 2022); the
+ * epilogue undoes the scaling exactly.  Each product is represented to about
+ * 2^-21 relative, so the result meets the fp32 bound 1e-5 * |a_i| * |b_j|
+ * (row and column 2-norms) by a wide margin; it is not bitwise equal to
+ * gemm_f32.  Non-finite inputs give NaN or Inf but not necessarily the same
+ * ones as gemm_f32.
+ *
+ *   workspace  device memory owned by the caller, 16-byte aligned, not
+ *              overlapping A, B or C, of at least
+ *              mg_split16_workspace_size(M, N, K) bytes (about 12 (M + N) K
+ *              bytes: the split operands); contents on entry are ignored.
+ * Errors: as for gemm_f32, plus MG_EINVAL for a missing, misaligned,
+ * overlapping or too small workspace, and MG_EUNSUPPORTED for M, N or K
+ * above 2^22, or K above 699040 (the split operands' row pitch). */
+mg_status gemm_f32_split16(mg_op ta, mg_op tb, int64_t M, int64_t N, int64_t K, float alpha,
+                           const float *A, int64_t lda, const float *B, int64_t ldb, float beta,
+                           float *C, int64_t ldc, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/* Workspace bytes gemm_f32_split16 needs (0 for an empty problem). */
+size_t mg_split16_workspace_size(int64_t M, int64_t N, int64_t K);
+
 /* Kernel configurations available for an input type, and their names
  * (static strings, e.g. "mfma_256x256x64_w2x2"). */
 int mg_num_configs(mg_dtype in_type);

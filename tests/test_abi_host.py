@@ -206,3 +206,35 @@ def test_workspace_size_matches_the_split_rule(mg):
     assert lib.mg_workspace_size(mg.MG_F32, mg.MG_F32, 0, 0, 0, 4096, 4096, 4096, 4096) == 0
     # short K: no split (each range must be at least two K slices)
     assert lib.mg_workspace_size(mg.MG_F32, mg.MG_F32, 0, 0, 64, 64, 64, 64, 64) == 0
+
+
+def s16(mg, M=64, N=64, K=256, ws=1 << 30, ws_bytes=None, A=FAKE_A, B=FAKE_B, C=FAKE_C):
+    lib = mg.load()
+    if ws_bytes is None:
+        ws_bytes = lib.mg_split16_workspace_size(M, N, K)
+    return lib.gemm_f32_split16(0, 0, M, N, K, 1.0, A, K, B, N, 0.0, C, N, ws, ws_bytes, None)
+
+
+def test_split16_workspace_size_closed_form(mg):
+    """Sections (each rounded up to 256 bytes): A' and B' at 3 Kp fp16 per
+    row (Kp = K rounded up to 64), one exponent per row and per column, and
+    partial column maxima for up to 16 K ranges."""
+    lib = mg.load()
+    up = lambda x: (x + 255) // 256 * 256
+    for (M, N, K) in ((64, 64, 256), (8192, 8192, 4096), (127, 4096, 4095), (5, 7, 3)):
+        kp = (K + 63) // 64 * 64
+        parts = min(16, max(1, K // 256))
+        want = up(M * 3 * kp * 2) + up(N * 3 * kp * 2) + up(M * 4) + up(N * 4) + up(parts * max(M, N) * 4)
+        assert lib.mg_split16_workspace_size(M, N, K) == want
+    assert lib.mg_split16_workspace_size(0, 8, 8) == 0
+
+
+def test_split16_arguments_are_rejected_before_launch(mg):
+    E = mg.MG_EINVAL
+    assert s16(mg, ws=None) == E
+    assert s16(mg, ws=(1 << 30) + 4) == E
+    assert s16(mg, ws_bytes=mg.load().mg_split16_workspace_size(64, 64, 256) - 256) == E
+    assert s16(mg, ws=FAKE_C) == E                      # overlaps C
+    assert s16(mg, M=-1) == E
+    assert s16(mg, K=(1 << 22) + 1, ws_bytes=1 << 62) == mg.MG_EUNSUPPORTED
+    assert s16(mg, M=0, ws=None, ws_bytes=0) == mg.MG_OK  # empty: nothing to do

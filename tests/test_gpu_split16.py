@@ -1,0 +1,136 @@
+"""fp32 GEMM through split fp16 inputs (gemm_f32_split16) against the oracle.
+
+The oracle is the plain fp64 definition; the split path must meet the fp32
+bound 1e-5 * |a_i| |b_j| on random data, on rows and columns whose scales
+differ by many orders of magnitude, and on magnitudes fp16 cannot hold
+without scaling.  On integer data every partial sum is a multiple of
+2^(e_m + f_n) with at most 15 significant bits, so the result must equal the
+oracle bit for bit.  All GPU work goes through the C ABI.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import gemm_inputs as gi
+from gpu_helpers import (assert_bit_exact, assert_within, freivalds_stream, log, oracle_cols, oracle_full,
+                         oracle_rows, out_as_f64, sample_plan, stored_shapes)
+
+pytestmark = pytest.mark.gpu
+
+LAYOUTS = list(itertools.product([False, True], repeat=2))  # (ta, tb)
+
+
+def run_split16(A, B, Cin, *, alpha, beta, ta, tb):
+    """Run gemm_f32_split16 with a guarded workspace; C on the host."""
+    import dense_gemm_12_amd as mg
+    dev = torch.device("cuda:0")
+    Ad, Bd = A.to(dev), B.to(dev)
+    M = A.shape[1] if ta else A.shape[0]
+    N = B.shape[0] if tb else B.shape[1]
+    K = A.shape[0] if ta else A.shape[1]
+    Cd = (Cin.to(dev) if Cin is not None else torch.full((M, N), float("nan"), device=dev))
+    need = mg.split16_workspace_size(M, N, K)
+    ws_all = torch.full((need + 256,), 0xFF, dtype=torch.uint8, device=dev)
+    ws_all[need:] = 0xAB
+    mg.gemm(Ad, Bd, Cd, alpha=alpha, beta=beta, trans_a=ta, trans_b=tb, split16=True,
+            workspace=ws_all[:need])
+    torch.cuda.synchronize()
+    assert torch.all(ws_all[need:] == 0xAB).item(), "split16 wrote past its workspace"
+    return Cd.cpu()
+
+
+def check(A, B, C, *, alpha, beta, ta, tb, exact, what):
+    log("case " + what)
+    Cin = C if beta != 0 else None
+    got = run_split16(A, B, Cin, alpha=alpha, beta=beta, ta=ta, tb=tb)
+    ref = oracle_full(A, B, Cin, alpha=alpha, beta=beta, ta=ta, tb=tb, in_dtype="f32", c_dtype="f32")
+    if exact:
+        assert_bit_exact(got, ref, "f32", what)
+        return 0.0
+    worst = assert_within(out_as_f64(got, "f32"), ref, A=A, B=B, Cin=C, alpha=alpha, beta=beta, ta=ta,
+                          tb=tb, in_dtype="f32", c_dtype="f32", what=what)
+    log(f"  worst error / bound = {worst:.3g}")
+    return worst
+
+
+def make(M, N, K, ta, tb, dist, seed):
+    sa, sb = stored_shapes(M, N, K, ta, tb)
+    return gi.draw(*sa, dist, seed, "f32"), gi.draw(*sb, dist, seed + 1, "f32"), gi.draw(M, N, dist, seed + 2, "f32")
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_integer_bit_exact_every_layout(ta, tb):
+    for (M, N, K) in ((200, 136, 300), (257, 129, 1000)):
+        A, B, C = make(M, N, K, ta, tb, "int2", 81)
+        check(A, B, C, alpha=1.5, beta=0.5, ta=ta, tb=tb, exact=True,
+              what=f"int ta={int(ta)} tb={int(tb)} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_random_within_fp32_bound(ta, tb):
+    for (M, N, K), dist in (((200, 136, 300), "uniform"), ((96, 160, 2000), "normal")):
+        A, B, C = make(M, N, K, ta, tb, dist, 91)
+        worst = check(A, B, C, alpha=1.0, beta=0.0, ta=ta, tb=tb, exact=False,
+                      what=f"{dist} ta={int(ta)} tb={int(tb)} {M}x{N}x{K}")
+        # the split keeps about 21 bits per product: far inside the bound
+        assert worst < 0.05
+
+
+def test_row_and_column_scales_far_apart():
+    """Rows of op(A) scaled by 2^-60 .. 2^60 and columns of op(B) by
+    2^-40 .. 2^40: each gets its own exponent, so each stays accurate
+    relative to its own norm."""
+    M, N, K = 128, 96, 512
+    A, B, C = make(M, N, K, False, False, "uniform", 101)
+    rs = torch.tensor([2.0 ** (((i * 37) % 121) - 60) for i in range(M)])
+    cs = torch.tensor([2.0 ** (((j * 29) % 81) - 40) for j in range(N)])
+    A = (A * rs[:, None]).contiguous()
+    B = (B * cs[None, :]).contiguous()
+    worst = check(A, B, C, alpha=1.0, beta=0.0, ta=False, tb=False, exact=False, what="scales 2^+-60 / 2^+-40")
+    assert worst < 0.05
+
+
+def test_magnitudes_below_fp16_range():
+    """Values around 1e-9 (below fp16's smallest subnormal, 6e-8) and around
+    1e30 (above its maximum) are exact powers of two away from the scaled
+    range, so the result keeps fp32 accuracy."""
+    M, N, K = 64, 64, 256
+    A, B, C = make(M, N, K, False, True, "uniform", 111)
+    for sa, sb in ((1e-9, 1e-9), (1e30, 1e-30), (3e-20, 7e15)):
+        check((A * sa).contiguous(), (B * sb).contiguous(), C, alpha=1.0, beta=0.0, ta=False, tb=True,
+              exact=False, what=f"magnitudes {sa:g} x {sb:g}")
+
+
+def test_zero_rows_and_columns():
+    M, N, K = 64, 80, 128
+    A, B, C = make(M, N, K, False, False, "uniform", 121)
+    A[5] = 0.0
+    B[:, 7] = 0.0
+    got = run_split16(A, B, None, alpha=1.0, beta=0.0, ta=False, tb=False)
+    assert torch.all(got[5] == 0.0) and torch.all(got[:, 7] == 0.0)
+    assert not torch.isnan(got).any()
+
+
+@pytest.mark.parametrize("integer_twin", [False, True])
+def test_benchmark_workload(integer_twin):
+    """fp32 NN 8192x8192x4096: sampled rows/columns/corner blocks against the
+    oracle, and Freivalds over the whole result."""
+    name = "fp32_nn_8192x8192x4096"
+    w = gi.WORKLOADS[name]
+    A, B, C = gi.workload_inputs(name, integer_twin=integer_twin)
+    M, N, K = w["M"], w["N"], w["K"]
+    log(f"case {name} split16 int={integer_twin}")
+    got = run_split16(A, B, C, alpha=w["alpha"], beta=w["beta"], ta=False, tb=False)
+    rows, cols, blocks = sample_plan(M, N, 7)
+    kw = dict(alpha=w["alpha"], beta=w["beta"], ta=False, tb=False, in_dtype="f32", c_dtype="f32")
+    ref_r = oracle_rows(A, B, C, rows, **kw)
+    ref_c = oracle_cols(A, B, C, cols, **kw)
+    g64 = out_as_f64(got, "f32")
+    if integer_twin:
+        assert np.array_equal(g64[rows], ref_r) and np.array_equal(g64[:, cols], ref_c)
+    else:
+        assert_within(g64[rows], ref_r, A=A, B=B, Cin=C, what="rows", rows=rows, **kw)
+        assert_within(g64[:, cols], ref_c, A=A, B=B, Cin=C, what="cols", cols=cols, **kw)
+    freivalds_stream(got, A, B, C, seed=3, exact=integer_twin, **kw)
