@@ -21,10 +21,13 @@ GEMM alone); the GPU clocks and power are read with rocm-smi while untimed
 steps run; and a cache-blocked CPU GEMM (cpu_gemm/, fp32 accumulation, all
 cores) runs the whole step as a second CPU baseline.  A workload whose tile
 grid leaves CUs idle runs through the split-K entry point with the
-workspace the planner asks for.
+workspace the planner asks for.  The fp32 part is also timed through
+gemm_f32_split16 (fp32 accuracy from split fp16 inputs on the fp16 matrix
+cores) and reported as "fp32_via_split_fp16", outside ``value``.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-                       [--cold-steps N] [--no-clocks] [--workload NAME ...]
+                       [--cold-steps N] [--no-clocks] [--split16-steps N]
+                       [--workload NAME ...]
 """
 from __future__ import annotations
 
@@ -179,6 +182,9 @@ def main():
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="extra steps with a 512 MiB cache scrub before each launch (0: skip)")
     ap.add_argument("--no-clocks", action="store_true", help="skip the rocm-smi clock reading")
+    ap.add_argument("--split16-steps", type=int, default=10,
+                    help="launches of the fp32 part through split fp16 inputs, reported beside the "
+                         "step (0: skip)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -270,6 +276,38 @@ def main():
         th.join()
         clocks = box.get("c")
 
+    split16 = None
+    f32_calls = [c for c in calls if c[1]["in_dtype"] == "f32"]
+    if args.split16_steps > 0 and f32_calls:
+        # The fp32 part again through gemm_f32_split16 (fp32 accuracy from
+        # fp16 matrix cores); reported beside the step, not in its value.
+        name, w, Ad, Bd, Cd, _ws = f32_calls[0]
+        wsb = mg.split16_workspace_size(w["M"], w["N"], w["K"])
+        ws16 = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        f = lambda: mg.gemm(Ad, Bd, Cd, alpha=w["alpha"], beta=w["beta"], trans_a=w["ta"],
+                            trans_b=w["tb"], stream=stream, split16=True, workspace=ws16)
+        for _ in range(2):
+            f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.split16_steps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.split16_steps
+        kp = (w["K"] + 63) // 64 * 64
+        mfma_flops = 2.0 * w["M"] * w["N"] * 3 * kp
+        split16 = {"workload": name, "entry": "gemm_f32_split16", "us_per_launch": round(ms * 1e3, 2),
+                   "tflops_algorithmic": round(flops(w) / (ms * 1e-3) / 1e12, 2),
+                   "fp16_mfma_flops_per_launch": mfma_flops,
+                   "fp16_mfma_tflops": round(mfma_flops / (ms * 1e-3) / 1e12, 2),
+                   "frac_of_fp16_peak": round(mfma_flops / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["f16"], 4),
+                   "workspace_bytes": wsb,
+                   "note": "fp32 result within 1e-5*|a_i||b_j| from split fp16 inputs; includes the "
+                           "split/scale passes; not part of value"}
+        del ws16
+
     step_flops = sum(flops(w) for _, w, *_ in calls)
     value = args.steps * step_flops / elapsed / 1e12
     parts = []
@@ -305,6 +343,7 @@ def main():
         "data": "synthetic: seeded fp32 N(0,1) and fp16 N(0,1)/sqrt(K) matrices, resident in HBM",
         "config": {"workload": " + ".join(names), "parts": list(names)},
         "parts": parts, "roofline": roofline, "gpu_clocks_under_load": clocks,
+        "fp32_via_split_fp16": split16,
     }
     if not args.no_cpu and rank == 0:
         log("CPU oracle baseline")

@@ -1,7 +1,9 @@
 """Build libmgemm.so in-tree with hipcc for gfx950.
 
 Every translation unit under ``csrc/`` is compiled in parallel, then linked
-into ``dense_gemm_12_amd/libmgemm.so``.  Run ``python -m dense_gemm_12_amd.build``.
+into ``dense_gemm_12_amd/libmgemm.so``.  Run ``python -m dense_gemm_12_amd.build``
+(``--changed``: recompile only sources older than their object files'
+dependencies).
 """
 from __future__ import annotations
 
@@ -41,8 +43,21 @@ def sources():
                   if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str, extra: list[str]) -> str:
+def _stale(src: str, obj: str) -> bool:
+    """An object is rebuilt when it is older than its source, any header
+    under csrc/, the public header or this script."""
+    if not os.path.exists(obj):
+        return True
+    deps = [src, __file__, os.path.join(os.path.dirname(HERE), "include", "mgemm.h")]
+    deps += [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hpp")]
+    t = os.path.getmtime(obj)
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+def _compile(src: str, extra: list[str], force: bool = True) -> str:
     obj = os.path.join(OUT_DIR, os.path.basename(src) + ".o")
+    if not force and not extra and not _stale(src, obj):
+        return obj
     cmd = [HIPCC, *COMMON, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -50,14 +65,16 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(jobs: int | None = None, extra: list[str] | None = None, verbose: bool = False) -> str:
-    """Compile every source and link the shared library; returns its path."""
+def build(jobs: int | None = None, extra: list[str] | None = None, verbose: bool = False,
+          force: bool = True) -> str:
+    """Compile every source (with force=False only the stale ones) and link
+    the shared library; returns its path."""
     os.makedirs(OUT_DIR, exist_ok=True)
     extra = list(extra or [])
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), srcs))
+        objs = list(ex.map(lambda s: _compile(s, extra, force), srcs))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -70,4 +87,4 @@ def build(jobs: int | None = None, extra: list[str] | None = None, verbose: bool
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, force="--changed" not in sys.argv)

@@ -321,7 +321,7 @@ static Split16Layout split16_layout(int64_t M, int64_t N, int64_t K) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   Split16Layout L{};
   L.Kp = (K + 63) / 64 * 64;
-  L.parts = (int)(K / 256 < 1 ? 1 : (K / 256 > 16 ? 16 : K / 256));
+  L.parts = (int)(K / 64 < 1 ? 1 : (K / 64 > 64 ? 64 : K / 64));
   L.a = 0;
   L.b = L.a + up((size_t)M * 3 * L.Kp * 2);
   L.re = L.b + up((size_t)N * 3 * L.Kp * 2);

@@ -26,6 +26,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "gfx950_prims.hpp"
 #include "split16.hpp"
 
 namespace mg {
@@ -73,9 +74,16 @@ __global__ void __launch_bounds__(kThreads) colmax_partial(const float *X, int64
   const int r = blockIdx.x * kThreads + threadIdx.x;
   if (r >= R) return;
   const int k0 = blockIdx.y * kchunk, k1 = min(K, k0 + kchunk);
-  float m = 0.0f;
-  for (int k = k0; k < k1; ++k) m = fmaxf(m, fabsf(X[(int64_t)k * ld + r]));
-  pm[(int64_t)blockIdx.y * R + r] = m;
+  float m0 = 0.0f, m1 = 0.0f, m2 = 0.0f, m3 = 0.0f;
+  int k = k0;
+  for (; k + 3 < k1; k += 4) {  // four independent loads in flight
+    m0 = fmaxf(m0, fabsf(X[(int64_t)k * ld + r]));
+    m1 = fmaxf(m1, fabsf(X[(int64_t)(k + 1) * ld + r]));
+    m2 = fmaxf(m2, fabsf(X[(int64_t)(k + 2) * ld + r]));
+    m3 = fmaxf(m3, fabsf(X[(int64_t)(k + 3) * ld + r]));
+  }
+  for (; k < k1; ++k) m0 = fmaxf(m0, fabsf(X[(int64_t)k * ld + r]));
+  pm[(int64_t)blockIdx.y * R + r] = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
 }
 
 __global__ void __launch_bounds__(kThreads) colmax_final(const float *pm, int R, int parts, int *exp_out) {
@@ -86,26 +94,38 @@ __global__ void __launch_bounds__(kThreads) colmax_final(const float *pm, int R,
   exp_out[r] = scale_exp(m);
 }
 
-// Writes the three segments of element (r, k) of the split operand.
+// Writes the three segments of elements (r, k .. k+3) of the split operand
+// (k a multiple of 4, so each segment store is one aligned 8-byte write).
 // pattern 0: [hi | hi | lo] (the A side); 1: [hi | lo | hi] (the B side).
-__device__ __forceinline__ void put(uint16_t *out, int64_t row_off, int Kp, int k, float v, int pattern) {
-  const _Float16 hi = (_Float16)v;
-  const _Float16 lo = (_Float16)(v - (float)hi);
-  const uint16_t h = __builtin_bit_cast(uint16_t, hi), l = __builtin_bit_cast(uint16_t, lo);
-  uint16_t *o = out + row_off + k;
-  o[0] = h;
-  o[Kp] = pattern == 0 ? h : l;
-  o[2 * Kp] = pattern == 0 ? l : h;
+__device__ __forceinline__ void put4(uint16_t *out, int64_t row_off, int Kp, int k, const float (&v)[4],
+                                     int pattern) {
+  uint32_t h[2], l[2];
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    const _Float16 h0 = (_Float16)v[2 * d], h1 = (_Float16)v[2 * d + 1];
+    const _Float16 l0 = (_Float16)(v[2 * d] - (float)h0), l1 = (_Float16)(v[2 * d + 1] - (float)h1);
+    h[d] = __builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+    l[d] = __builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+  }
+  u32x2 *o = reinterpret_cast<u32x2 *>(out + row_off + k);
+  const u32x2 hv = {h[0], h[1]}, lv = {l[0], l[1]};
+  o[0] = hv;
+  *reinterpret_cast<u32x2 *>(out + row_off + Kp + k) = pattern == 0 ? hv : lv;
+  *reinterpret_cast<u32x2 *>(out + row_off + 2 * Kp + k) = pattern == 0 ? lv : hv;
 }
 
-// Row-contiguous source: grid (R, ceil(Kp / kThreads)), thread per k.
+// Row-contiguous source: grid (R, ceil(Kp / (4 kThreads))), four k per thread.
 __global__ void __launch_bounds__(kThreads) split_direct(const float *X, int64_t ld, int K, int Kp,
                                                          const int *exps, uint16_t *out, int pattern) {
   const int r = blockIdx.x;
-  const int k = blockIdx.y * kThreads + threadIdx.x;
+  const int k = (blockIdx.y * kThreads + threadIdx.x) * 4;
   if (k >= Kp) return;
-  const float v = k < K ? ldexpf(X[(int64_t)r * ld + k], exps[r]) : 0.0f;
-  put(out, (int64_t)r * 3 * Kp, Kp, k, v, pattern);
+  const float *row = X + (int64_t)r * ld;
+  const int e = exps[r];
+  float v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = k + i < K ? ldexpf(row[k + i], e) : 0.0f;
+  put4(out, (int64_t)r * 3 * Kp, Kp, k, v, pattern);
 }
 
 // Column source (stored K x R): 64 x 64 tiles through LDS so that both the
@@ -121,9 +141,17 @@ __global__ void __launch_bounds__(kThreads) split_transposed(const float *X, int
     tile[kk][tx] = (k < K && r < R) ? X[(int64_t)k * ld + r] : 0.0f;
   }
   __syncthreads();
-  for (int rr = ty; rr < 64; rr += 4) {
-    const int r = r0 + rr, k = k0 + tx;
-    if (r < R && k < Kp) put(out, (int64_t)r * 3 * Kp, Kp, k, ldexpf(tile[tx][rr], exps[r]), pattern);
+  // 16 threads per row, four k each; 16 rows per pass
+  const int kq = (threadIdx.x & 15) * 4, rr0 = threadIdx.x >> 4;
+  for (int rr = rr0; rr < 64; rr += 16) {
+    const int r = r0 + rr, k = k0 + kq;
+    if (r < R && k < Kp) {
+      const int e = exps[r];
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = ldexpf(tile[kq + i][rr], e);
+      put4(out, (int64_t)r * 3 * Kp, Kp, k, v, pattern);
+    }
   }
 }
 
@@ -145,7 +173,8 @@ hipError_t split16_prepare(const Split16Plan &s, hipStream_t stream) {
   auto split = [&](const float *X, int64_t ld, int R, bool contiguous, const int *e, uint16_t *out,
                    int pattern) {
     if (contiguous)
-      hipLaunchKernelGGL(split_direct, dim3(R, (s.Kp + kThreads - 1) / kThreads), dim3(kThreads), 0, stream,
+      hipLaunchKernelGGL(split_direct, dim3(R, (s.Kp + 4 * kThreads - 1) / (4 * kThreads)), dim3(kThreads), 0,
+                         stream,
                          X, ld, s.K, s.Kp, e, out, pattern);
     else
       hipLaunchKernelGGL(split_transposed, dim3((s.Kp + 63) / 64, (R + 63) / 64), dim3(kThreads), 0, stream,

@@ -223,7 +223,7 @@ def test_split16_workspace_size_closed_form(mg):
     up = lambda x: (x + 255) // 256 * 256
     for (M, N, K) in ((64, 64, 256), (8192, 8192, 4096), (127, 4096, 4095), (5, 7, 3)):
         kp = (K + 63) // 64 * 64
-        parts = min(16, max(1, K // 256))
+        parts = min(64, max(1, K // 64))
         want = up(M * 3 * kp * 2) + up(N * 3 * kp * 2) + up(M * 4) + up(N * 4) + up(parts * max(M, N) * 4)
         assert lib.mg_split16_workspace_size(M, N, K) == want
     assert lib.mg_split16_workspace_size(0, 8, 8) == 0
