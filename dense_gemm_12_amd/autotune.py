@@ -10,10 +10,13 @@ Each configuration gets a warm-up, then ``--trials`` timed runs of enough
 launches to pass ``--min-ms``, timed with HIP events on the launch stream;
 the median trial decides.  Table rows are
 
-    <in> <c> <ta> <tb> <M> <N> <K> <config>
+    <in> <c> <ta> <tb> <M> <N> <K> <config> [ws]
 
 and the library matches a problem to the nearest row of the same type and
-layout class (log-distance in M, N, K).  The per-configuration timings are
+layout class (log-distance in M, N, K).  Rows tagged ``ws`` were tuned
+through gemm_ex with a workspace (split-K and operand repacking allowed) and
+apply only to such calls; a workload gets one when the planner would split
+or repack it.  The per-configuration timings are
 kept as comments.
 """
 from __future__ import annotations
@@ -29,10 +32,10 @@ ROOT = os.path.dirname(HERE)
 sys.path.insert(0, ROOT)
 
 
-def time_config(mg, torch, A, B, C, w, cfg, trials, min_ms):
+def time_config(mg, torch, A, B, C, w, cfg, trials, min_ms, workspace=None):
     stream = torch.cuda.current_stream()
     call = lambda: mg.gemm(A, B, C, alpha=w["alpha"], beta=w["beta"], trans_a=w["ta"],
-                           trans_b=w["tb"], config=cfg, stream=stream)
+                           trans_b=w["tb"], config=cfg, stream=stream, workspace=workspace)
     call()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -63,32 +66,41 @@ def tune(names, out, trials=3, min_ms=20.0, log=print):
     mg.load()
     dev = torch.device("cuda:0")
     lines = ["# dense_gemm_12_amd tuning table for gfx950 (MI355X); written by autotune.py",
-             "# <in> <c> <ta> <tb> <M> <N> <K> <config>; comments: the three fastest candidates"]
+             "# <in> <c> <ta> <tb> <M> <N> <K> <config> [ws]; comments: the three fastest candidates"]
     for name in names:
         w = gi.WORKLOADS[name]
         A, B, C = gi.workload_inputs(name)
         Ad, Bd = A.to(dev), B.to(dev)
         Cd = (C.to(dev) if C is not None else
               torch.zeros((w["M"], w["N"]), dtype=gi.DTYPES[w["c_dtype"]], device=dev))
-        results = []
-        for cfg in range(mg.num_configs(w["in_dtype"])):
-            cname = mg.config_name(w["in_dtype"], cfg)
-            try:
-                ms = time_config(mg, torch, Ad, Bd, Cd, w, cfg, trials, min_ms)
-            except mg.MgemmError as e:
-                if e.status != mg.MG_EUNSUPPORTED:
-                    raise
+        codes = mg.DTYPE_CODES
+        wsb = mg.workspace_size(codes[w["in_dtype"]], codes[w["c_dtype"]], int(w["ta"]), int(w["tb"]),
+                                w["M"], w["N"], w["K"], Ad.stride(0), Bd.stride(0))
+        # plain calls, then (when gemm_ex would split or repack) calls with a
+        # workspace, each tuned into its own rule
+        passes = [("", None)]
+        if wsb:
+            passes.append((" ws", torch.empty(wsb, dtype=torch.uint8, device=dev)))
+        for tag, ws in passes:
+            results = []
+            for cfg in range(mg.num_configs(w["in_dtype"])):
+                cname = mg.config_name(w["in_dtype"], cfg)
+                try:
+                    ms = time_config(mg, torch, Ad, Bd, Cd, w, cfg, trials, min_ms, workspace=ws)
+                except mg.MgemmError as e:
+                    if e.status != mg.MG_EUNSUPPORTED:
+                        raise
+                    continue
+                flops = 2.0 * w["M"] * w["N"] * w["K"]
+                results.append((ms, cname))
+                log(f"{name + tag:28s} {cname:32s} {ms * 1e3:10.1f} us {flops / ms / 1e9:9.1f} TFLOPS")
+            if not results:
                 continue
-            flops = 2.0 * w["M"] * w["N"] * w["K"]
-            results.append((ms, cname))
-            log(f"{name:28s} {cname:32s} {ms * 1e3:10.1f} us {flops / ms / 1e9:9.1f} TFLOPS")
-        if not results:
-            continue
-        results.sort()
-        best = results[0][1]
-        lines.append(f"# {name}: " + ", ".join(f"{c}={ms * 1e3:.1f}us" for ms, c in results[:3]))
-        lines.append(f"{w['in_dtype']} {w['c_dtype']} {'T' if w['ta'] else 'N'} {'T' if w['tb'] else 'N'} "
-                     f"{w['M']} {w['N']} {w['K']} {best}")
+            results.sort()
+            best = results[0][1]
+            lines.append(f"# {name}{tag}: " + ", ".join(f"{c}={ms * 1e3:.1f}us" for ms, c in results[:3]))
+            lines.append(f"{w['in_dtype']} {w['c_dtype']} {'T' if w['ta'] else 'N'} {'T' if w['tb'] else 'N'} "
+                         f"{w['M']} {w['N']} {w['K']} {best}{tag}")
         del Ad, Bd, Cd
         torch.cuda.empty_cache()
     tmp = out + ".tmp"

@@ -26,6 +26,7 @@
 // ends up owning 4 consecutive columns of one row of C and stores them with a
 // single 16- or 8-byte write.
 #pragma once
+#include <type_traits>
 #include "gemm_params.hpp"
 #include "epilogue.hpp"
 #include "gfx950_prims.hpp"
@@ -296,6 +297,24 @@ __global__ void __launch_bounds__(256) scale_c_kernel(GemmParams p) {
     // alpha * (empty or ignored product) contributes +0: 0 + beta*C (so a
     // -0 product beta*C becomes +0, as in the formula's left-to-right sum).
     *c = from_f32<TO>(p.beta == 0.0f ? 0.0f : 0.0f + p.beta * to_f32(*c));
+  }
+}
+
+// Operand repack: rows x cols elements of ES bytes at src (row pitch ld
+// elements) copied to dst with row pitch `pitch` (a multiple of 16 bytes),
+// columns cols .. pitch-1 zero.  The copy is 16-byte loadable, and the
+// zeros make a chunk that straddles the last column safe to read.
+template <int ES>
+__global__ void __launch_bounds__(256) pack_rows_kernel(const void *src, int64_t ld, int64_t rows,
+                                                        int64_t cols, void *dst, int64_t pitch) {
+  typedef typename std::conditional<ES == 4, uint32_t, uint16_t>::type T;
+  const T *s = static_cast<const T *>(src);
+  T *d = static_cast<T *>(dst);
+  const int64_t total = rows * pitch;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / pitch, c = i - r * pitch;
+    d[i] = c < cols ? s[r * ld + c] : (T)0;
   }
 }
 

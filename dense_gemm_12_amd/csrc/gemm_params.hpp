@@ -53,5 +53,9 @@ const KernelEntry *entries_bf16(int *n);
 
 LaunchFn scale_launcher(int c_dtype);   // 0 = f32, 1 = f16, 2 = bf16
 LaunchFn reduce_launcher(int c_dtype);  // split-K partial sums -> C, same codes
+// Copies a rows x cols operand (es-byte elements) into a zero-padded buffer
+// with a 16-byte-multiple row pitch.
+hipError_t launch_pack(int es, const void *src, int64_t ld, int64_t rows, int64_t cols, void *dst,
+                       int64_t pitch, hipStream_t s);
 
 }  // namespace mg

@@ -53,6 +53,21 @@ LaunchFn reduce_launcher(int c_dtype) {
   }
 }
 
+hipError_t launch_pack(int es, const void *src, int64_t ld, int64_t rows, int64_t cols, void *dst,
+                       int64_t pitch, hipStream_t s) {
+  const int64_t total = rows * pitch;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) return hipSuccess;
+  if (es == 4)
+    hipLaunchKernelGGL(pack_rows_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s, src, ld, rows, cols, dst,
+                       pitch);
+  else
+    hipLaunchKernelGGL(pack_rows_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s, src, ld, rows, cols, dst,
+                       pitch);
+  return hipGetLastError();
+}
+
 LaunchFn scale_launcher(int c_dtype) {
   switch (c_dtype) {
     case 0: return &launch_scale<float>;

@@ -43,6 +43,7 @@ struct Rule {
   int in, c, ta, tb;
   int64_t M, N, K;
   std::string config;
+  bool ws;  // tuned for the workspace path (split-K and operand repacking allowed)
 };
 std::vector<Rule> g_rules;  // read-only after mg_load_tune_table
 
@@ -68,6 +69,10 @@ struct Problem {
   float alpha, beta;
   const void *A, *B;
   void *C;
+  // A or B is a zero-padded copy made by the library (16-byte loads legal
+  // even when the contiguous extent is not a whole number of chunks).
+  bool a_padded = false, b_padded = false;
+  bool ws_path = false;  // planning for a call that has a workspace
 };
 
 bool ranges_overlap(const void *p, int64_t pbytes, const void *q, int64_t qbytes) {
@@ -112,10 +117,17 @@ mg_status validate(const Problem &p) {
   return MG_OK;
 }
 
-// 16-byte loads along an operand's contiguous dimension are legal.
-bool vec_ok(const void *base, int64_t ld, int64_t contiguous_extent, int es) {
+// 16-byte loads along an operand's contiguous dimension are legal: aligned
+// base and pitch, and either whole chunks or a zero-padded library copy.
+bool vec_ok(const void *base, int64_t ld, int64_t contiguous_extent, int es, bool padded) {
   const int v = 16 / es;
-  return ((uintptr_t)base % 16 == 0) && ((ld * es) % 16 == 0) && (contiguous_extent % v == 0);
+  return ((uintptr_t)base % 16 == 0) && ((ld * es) % 16 == 0) && (padded || contiguous_extent % v == 0);
+}
+bool a_vec_ok(const Problem &p) {
+  return vec_ok(p.A, p.lda, p.ta == MG_N ? p.K : p.M, elem_size(p.in_type), p.a_padded);
+}
+bool b_vec_ok(const Problem &p) {
+  return vec_ok(p.B, p.ldb, p.tb == MG_T ? p.K : p.N, elem_size(p.in_type), p.b_padded);
 }
 
 // ------------------------------------------------------------- planning --
@@ -153,11 +165,11 @@ int heuristic_config(const Problem &p) {
   return best;
 }
 
-int table_config(const Problem &p) {
+int table_config(const Problem &p, bool ws_rules) {
   const Rule *best = nullptr;
   double best_d = 1e300;
   for (const Rule &r : g_rules) {
-    if (r.in != p.in_type || r.c != p.c_type || r.ta != p.ta || r.tb != p.tb) continue;
+    if (r.in != p.in_type || r.c != p.c_type || r.ta != p.ta || r.tb != p.tb || r.ws != ws_rules) continue;
     const double d = fabs(log2((double)(p.M + 1) / (r.M + 1))) +
                      fabs(log2((double)(p.N + 1) / (r.N + 1))) +
                      fabs(log2((double)(p.K + 1) / (r.K + 1)));
@@ -180,17 +192,21 @@ int elem_config(int in_type, bool a_vec, bool b_vec) {
 }
 
 Plan plan(const Problem &p) {
-  const int es = elem_size(p.in_type);
   const bool a_kc = p.ta == MG_N, b_kc = p.tb == MG_T;
   Plan pl;
-  pl.a_vec = vec_ok(p.A, p.lda, a_kc ? p.K : p.M, es);
-  pl.b_vec = vec_ok(p.B, p.ldb, b_kc ? p.K : p.N, es);
+  pl.a_vec = a_vec_ok(p);
+  pl.b_vec = b_vec_ok(p);
   if (pl.a_vec && pl.b_vec) {
-    int c = table_config(p);
+    int c = p.ws_path ? table_config(p, true) : -1;
+    if (c < 0) c = table_config(p, false);
     if (c >= 0) {
+      // a rule naming an element-load variant was tuned on operands 16-byte
+      // loads could not read; these can be, so the rule does not apply
       int n = 0;
       const KernelEntry *e = entries(p.in_type, &n);
-      if (e[c].fn[p.c_type == MG_F32 ? 1 : 0][a_kc ? 1 : 0][b_kc ? 1 : 0] == nullptr) c = -1;
+      if (e[c].fn[p.c_type == MG_F32 ? 1 : 0][a_kc ? 1 : 0][b_kc ? 1 : 0] == nullptr || !e[c].a_vec ||
+          !e[c].b_vec)
+        c = -1;
     }
     pl.config = c >= 0 ? c : heuristic_config(p);
   } else {
@@ -227,6 +243,30 @@ static int auto_splits(const Problem &p, const KernelEntry &k, int64_t ws_bytes)
   if (s > by_ws) s = by_ws;
   if (s > kMaxSplits) s = kMaxSplits;
   return s < 2 ? 1 : (int)s;
+}
+
+// Operand repacking for the workspace path: an operand that 16-byte loads
+// cannot read (misaligned base or pitch, or a contiguous extent that is not
+// a whole number of chunks) is copied into the workspace with its pitch
+// rounded up to a chunk and the padding zeroed.  Returns the bytes the copy
+// takes (0 when the operand is already loadable or cannot be repacked).
+struct Pack {
+  int64_t rows, cols, pitch;
+  size_t bytes;
+};
+
+static Pack pack_shape(const Problem &p, bool is_a) {
+  Pack k{0, 0, 0, 0};
+  if (is_a ? a_vec_ok(p) : b_vec_ok(p)) return k;
+  const int es = elem_size(p.in_type), v = 16 / es;
+  const bool kc = is_a ? p.ta == MG_N : p.tb == MG_T;
+  const int64_t outer = is_a ? p.M : p.N;
+  k.rows = kc ? outer : p.K;
+  k.cols = kc ? p.K : outer;
+  k.pitch = (k.cols + v - 1) / v * v;
+  if (k.pitch > kMaxLd || k.rows <= 0 || k.cols <= 0) return Pack{0, 0, 0, 0};
+  k.bytes = ((size_t)k.rows * k.pitch * es + 255) / 256 * 256;
+  return k;
 }
 
 // Implementation shared by the entry points.  splits: 0 = planner's choice
@@ -278,6 +318,36 @@ static mg_status run(const Problem &p, int forced, int splits, void *ws, size_t 
   hipError_t err;
   if (p.K == 0 || p.alpha == 0.0f) {
     err = mg::scale_launcher(c_idx)(gp, stream);
+  } else if (ws_bytes > 0 && !(p.ws_path)) {
+    // Workspace path: repack what 16-byte loads cannot read (keeping room
+    // for a forced split), then plan and split with the rest.
+    Problem q = p;
+    q.ws_path = true;
+    char *w = static_cast<char *>(ws);
+    size_t used = 0;
+    const size_t reserve = splits > 1 ? (size_t)splits * p.M * p.N * 4 : 0;
+    for (int side = 0; side < 2; ++side) {
+      const Pack k = pack_shape(q, side == 0);
+      if (k.bytes == 0 || used + k.bytes + reserve > ws_bytes) continue;
+      const void *src = side == 0 ? q.A : q.B;
+      const int64_t ld = side == 0 ? q.lda : q.ldb;
+      err = mg::launch_pack(elem_size(q.in_type), src, ld, k.rows, k.cols, w + used, k.pitch, stream);
+      if (err != hipSuccess) {
+        g_last_hip_error = (int)err;
+        return MG_EHIP;
+      }
+      if (side == 0) {
+        q.A = w + used;
+        q.lda = k.pitch;
+        q.a_padded = true;
+      } else {
+        q.B = w + used;
+        q.ldb = k.pitch;
+        q.b_padded = true;
+      }
+      used += k.bytes;
+    }
+    return run(q, forced, splits, w + used, ws_bytes - used, stream_v, row_exp, col_exp);
   } else {
     Plan pl = plan(p);
     int cfg = forced >= 0 ? forced : pl.config;
@@ -450,13 +520,27 @@ size_t mg_workspace_size(mg_dtype in_type, mg_dtype c_type, mg_op ta, mg_op tb, 
   // Planned as for 16-byte-aligned base pointers with the given leading dimensions.
   Problem p{(int)in_type, (int)c_type, (int)ta, (int)tb, M, N, K, lda, ldb, N, 1.0f, 0.0f,
             (const void *)(uintptr_t)4096, (const void *)(uintptr_t)4096, nullptr};
+  p.ws_path = true;
+  size_t packed = 0;
+  for (int side = 0; side < 2; ++side) {
+    const Pack k = pack_shape(p, side == 0);
+    if (k.bytes == 0) continue;
+    packed += k.bytes;
+    if (side == 0) {
+      p.lda = k.pitch;
+      p.a_padded = true;
+    } else {
+      p.ldb = k.pitch;
+      p.b_padded = true;
+    }
+  }
   const int cfg = plan(p).config;
-  if (cfg < 0) return 0;
+  if (cfg < 0) return packed;
   int n = 0;
   const KernelEntry &k = entries(p.in_type, &n)[cfg];
   int chunk = 0;
   const int sp = split_shape(K, k.bk, auto_splits(p, k, INT64_MAX), &chunk);
-  return sp > 1 ? (size_t)sp * (size_t)M * (size_t)N * 4 : 0;
+  return packed + (sp > 1 ? (size_t)sp * (size_t)M * (size_t)N * 4 : 0);
 }
 
 int mg_num_configs(mg_dtype in_type) {
@@ -499,9 +583,11 @@ mg_status mg_load_tune_table(const char *path) {
       ok = false;
       break;
     }
-    char in[16], c[16], ta[4], tb[4], cfg[128];
+    char in[16], c[16], ta[4], tb[4], cfg[128], tag[8] = {0};
     long long M, N, K;
-    if (sscanf(line, "%15s %15s %3s %3s %lld %lld %lld %127s", in, c, ta, tb, &M, &N, &K, cfg) != 8) {
+    const int got = sscanf(line, "%15s %15s %3s %3s %lld %lld %lld %127s %7s", in, c, ta, tb, &M, &N, &K, cfg,
+                           tag);
+    if (got < 8 || (got == 9 && strcmp(tag, "ws") != 0)) {
       ok = false;
       break;
     }
@@ -514,6 +600,7 @@ mg_status mg_load_tune_table(const char *path) {
     r.N = N;
     r.K = K;
     r.config = cfg;
+    r.ws = got == 9;
     if (r.in < 0 || r.c < 0 || r.ta < 0 || r.tb < 0 || find_config(r.in, cfg) < 0) {
       ok = false;
       break;

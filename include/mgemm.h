@@ -122,6 +122,13 @@ mg_status gemm_bf16_cfg(int config, mg_op ta, mg_op tb, int64_t M, int64_t N, in
  *              workspace_bytes is 0.  Its contents on entry are ignored; it
  *              is scratch until the call's kernels have finished.
  *   config     as for the _cfg entry points (-1: the planner's choice).
+ *
+ * With a workspace, an operand that 16-byte loads cannot read (base or
+ * leading dimension not 16-byte aligned, or a contiguous extent that is not a
+ * multiple of 16 bytes) is first copied into the workspace with its rows
+ * padded with zeros to a 16-byte multiple, so the fast tiles run on it; the
+ * copies are placed first, then the split partials.  mg_workspace_size
+ * counts both (for 16-byte-aligned base pointers).
  * Errors: as above, plus MG_EINVAL for splits outside 0..64, a misaligned or
  * overlapping workspace, or one smaller than a forced split count needs. */
 mg_status gemm_ex(mg_dtype in_type, mg_dtype c_type, mg_op ta, mg_op tb, int64_t M, int64_t N,
@@ -130,8 +137,9 @@ mg_status gemm_ex(mg_dtype in_type, mg_dtype c_type, mg_op ta, mg_op tb, int64_t
                   int config, int splits, void *stream);
 
 /* Workspace bytes that gemm_ex with splits = 0 uses for this problem when
- * given enough (0 when it would not split), for 16-byte-aligned base
- * pointers with these leading dimensions. */
+ * given enough (operand copies plus split partials; 0 when it would neither
+ * repack nor split), for 16-byte-aligned base pointers with these leading
+ * dimensions. */
 size_t mg_workspace_size(mg_dtype in_type, mg_dtype c_type, mg_op ta, mg_op tb, int64_t M, int64_t N,
                          int64_t K, int64_t lda, int64_t ldb);
 
@@ -178,13 +186,16 @@ int mg_chosen_config(mg_dtype in_type, mg_dtype c_type, mg_op ta, mg_op tb, int6
                      int64_t K);
 
 /* Load a shape-keyed tuning table (text, one rule per line:
- * "<in> <c> <ta> <tb> <M> <N> <K> <config-name>", e.g. "f16 f16 N T 4096 4096 4096
- * mfma_256x256x64_w2x2"); lines starting with '#' are comments.  Exact shape
- * matches win; otherwise the nearest rule of the same type/layout class by
- * log-distance of M, N, K.  Replaces any table loaded before.  Returns
- * MG_EINVAL if the file cannot be read or a line names an unknown config
- * (the previous table is then kept).  Not safe to call concurrently with
- * GEMM calls. */
+ * "<in> <c> <ta> <tb> <M> <N> <K> <config-name> [ws]", e.g. "f16 f16 N T 4096 4096 4096
+ * dma_f16_256x256x64_s2_w2x4"); lines starting with '#' are comments.  A rule
+ * tagged "ws" applies only to gemm_ex calls with a workspace (it was tuned
+ * with split-K and operand repacking available); untagged rules apply to
+ * every call.  A problem takes the nearest rule of the same type and layout
+ * class by log-distance of M, N, K, if one is near enough; rules naming an
+ * element-load variant are skipped for operands 16-byte loads can read.
+ * Replaces any table loaded before.  Returns MG_EINVAL if the file cannot be
+ * read or a line names an unknown config or tag (the previous table is then
+ * kept).  Not safe to call concurrently with GEMM calls. */
 mg_status mg_load_tune_table(const char *path);
 /* Number of rules in the loaded table (0 if none). */
 int mg_tune_table_size(void);

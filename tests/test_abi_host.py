@@ -151,6 +151,17 @@ def test_tune_table_load_and_reject(mg, tmp_path):
     assert mg.load().mg_tune_table_size() == 1  # previous table kept
     with pytest.raises(mg.MgemmError):
         mg.load_tune_table(str(tmp_path / "missing.txt"))
+    # a "ws" rule applies only to workspace calls; an unknown tag is rejected
+    tagged = tmp_path / "ws.txt"
+    other = mg.config_name("f16", 4)
+    tagged.write_text(f"f16 f16 N T 4096 4096 4096 {name}\nf16 f16 N T 4096 4096 4096 {other} ws\n")
+    mg.load_tune_table(str(tagged))
+    assert mg.load().mg_tune_table_size() == 2
+    assert mg.chosen_config("f16", "f16", 0, 1, 4096, 4096, 4096) == 3
+    badtag = tmp_path / "badtag.txt"
+    badtag.write_text(f"f16 f16 N T 4096 4096 4096 {name} wsx\n")
+    with pytest.raises(mg.MgemmError):
+        mg.load_tune_table(str(badtag))
     # restore the packaged table (or none)
     empty = tmp_path / "empty.txt"
     empty.write_text("")
@@ -196,12 +207,18 @@ def test_split_k_arguments_are_rejected_before_launch(mg):
 
 
 def test_workspace_size_matches_the_split_rule(mg):
-    """The planner splits only when the tile grid leaves CUs idle: the odd-K
-    bf16 problem (one 128-row tile row of 32 tiles) takes 8 ranges of 512;
-    a 4096^3 problem never splits."""
+    """The planner splits only when the tile grid leaves CUs idle, and
+    repacks an operand 16-byte loads cannot read: the odd-K bf16 problem
+    (A rows of 4095 elements) needs A's zero-padded copy (127 rows, pitch
+    4096) plus at least two fp32 partials; an aligned copy of the same shape
+    needs no repack; a 4096^3 problem never splits."""
     lib = mg.load()
-    w = lib.mg_workspace_size(mg.MG_BF16, mg.MG_F32, 0, 0, 127, 4096, 4095, 4095, 4096)
-    assert w == 8 * 127 * 4096 * 4
+    M, N, K = 127, 4096, 4095
+    w = lib.mg_workspace_size(mg.MG_BF16, mg.MG_F32, 0, 0, M, N, K, 4095, 4096)
+    packed = M * 4096 * 2
+    assert w >= packed + 2 * M * N * 4 and (w - packed) % (M * N * 4) == 0
+    w2 = lib.mg_workspace_size(mg.MG_BF16, mg.MG_F32, 0, 0, M, N, 4096, 4096, 4096)
+    assert w2 % (M * N * 4) == 0 and w2 >= 2 * M * N * 4
     assert lib.mg_workspace_size(mg.MG_F16, mg.MG_F16, 0, 1, 4096, 4096, 4096, 4096, 4096) == 0
     assert lib.mg_workspace_size(mg.MG_F32, mg.MG_F32, 0, 0, 0, 4096, 4096, 4096, 4096) == 0
     # short K: no split (each range must be at least two K slices)

@@ -133,3 +133,27 @@ def test_c5b_workload_auto_split(integer_twin):
     else:
         assert_within(out_as_f64(got, "f32"), ref, A=A, B=B, Cin=C, alpha=w["alpha"], beta=w["beta"],
                       ta=False, tb=False, in_dtype="bf16", c_dtype="f32", what=name)
+
+
+@pytest.mark.parametrize("in_dtype", ["f32", "f16", "bf16"])
+def test_repacked_operands_integer_bit_exact(in_dtype):
+    """Operands 16-byte loads cannot read (odd contiguous extent, odd pitch,
+    base off by one element) are repacked into the workspace and run on the
+    vector tiles, split or not: every layout, bit-exact on integer data."""
+    import dense_gemm_12_amd as mg
+    c_dtype = "f32" if in_dtype != "bf16" else "bf16"
+    for (M, N, K), pad, off in (((127, 256, 1023), 0, 0), ((100, 90, 301), 3, 0), ((64, 72, 200), 0, 1)):
+        for (ta, tb) in LAYOUTS:
+            what = f"repack {in_dtype} ta={int(ta)} tb={int(tb)} {M}x{N}x{K} pad={pad} off={off}"
+            log("case " + what)
+            sa, sb = stored_shapes(M, N, K, ta, tb)
+            A = gi.draw(*sa, "int2", 131, in_dtype, ld=sa[1] + pad if pad else None)
+            B = gi.draw(*sb, "int2", 132, in_dtype, ld=sb[1] + pad if pad else None)
+            C = gi.draw(M, N, "int2", 133, c_dtype)
+            es = 4 if in_dtype == "f32" else 2
+            ws = (sa[0] * (sa[1] + 8) + sb[0] * (sb[1] + 8)) * es + 4096 + 16 * M * N * 4
+            got = run_gpu(A, B, C, alpha=1.5, beta=0.5, ta=ta, tb=tb, c_dtype=c_dtype, offset_elems=off,
+                          workspace_bytes=ws, splits=0)
+            ref = oracle_full(A, B, C, alpha=1.5, beta=0.5, ta=ta, tb=tb, in_dtype=in_dtype, c_dtype=c_dtype)
+            assert_bit_exact(got, ref, c_dtype, what)
+    assert mg.load() is not None
