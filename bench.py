@@ -313,8 +313,12 @@ def main():
     parts = []
     for i, (name, w, *_r) in enumerate(calls):
         ms = sum(events[k][i][0].elapsed_time(events[k][i][1]) for k in range(args.steps)) / args.steps
-        cfg = mg.chosen_config(w["in_dtype"], w["c_dtype"], int(w["ta"]), int(w["tb"]), w["M"],
-                               w["N"], w["K"])
+        if calls[i][5] is not None:  # the workspace path (split-K / repacked operands)
+            cfg = mg.chosen_config_ws(w["in_dtype"], w["c_dtype"], int(w["ta"]), int(w["tb"]), w["M"],
+                                      w["N"], w["K"], calls[i][2].stride(0), calls[i][3].stride(0))
+        else:
+            cfg = mg.chosen_config(w["in_dtype"], w["c_dtype"], int(w["ta"]), int(w["tb"]), w["M"],
+                                   w["N"], w["K"])
         tf = flops(w) / (ms * 1e-3) / 1e12
         parts.append({"workload": name, "kernel": mg.config_name(w["in_dtype"], cfg),
                       "us_per_launch": round(ms * 1e3, 2), "tflops": round(tf, 2),

@@ -26,7 +26,8 @@ DTYPE_CODES = {"f32": MG_F32, "f16": MG_F16, "bf16": MG_BF16}
 # Every exported symbol of include/mgemm.h.
 EXPORTS = (
     "gemm_f32", "gemm_f16", "gemm_bf16", "gemm_f32_cfg", "gemm_f16_cfg", "gemm_bf16_cfg",
-    "gemm_ex", "mg_workspace_size", "gemm_f32_split16", "mg_split16_workspace_size", "mg_num_configs", "mg_config_name", "mg_chosen_config", "mg_load_tune_table",
+    "gemm_ex", "mg_workspace_size", "gemm_f32_split16", "mg_split16_workspace_size", "mg_chosen_config_ws",
+    "mg_num_configs", "mg_config_name", "mg_chosen_config", "mg_load_tune_table",
     "mg_tune_table_size", "mg_status_str", "mg_last_hip_error", "mg_version",
 )
 
@@ -75,6 +76,8 @@ def load(path: str | None = None):
         lib.gemm_f32_split16.restype = ci
         lib.mg_split16_workspace_size.argtypes = [i64, i64, i64]
         lib.mg_split16_workspace_size.restype = ctypes.c_size_t
+        lib.mg_chosen_config_ws.argtypes = [ci, ci, ci, ci, i64, i64, i64, i64, i64]
+        lib.mg_chosen_config_ws.restype = ci
         lib.mg_num_configs.argtypes = [ci]
         lib.mg_num_configs.restype = ci
         lib.mg_config_name.argtypes = [ci, ci]
@@ -174,6 +177,10 @@ def config_id(in_type: str, name: str) -> int:
 
 def chosen_config(in_type, c_type, ta, tb, M, N, K) -> int:
     return load().mg_chosen_config(DTYPE_CODES[in_type], DTYPE_CODES[c_type], ta, tb, M, N, K)
+
+
+def chosen_config_ws(in_type, c_type, ta, tb, M, N, K, lda, ldb) -> int:
+    return load().mg_chosen_config_ws(DTYPE_CODES[in_type], DTYPE_CODES[c_type], ta, tb, M, N, K, lda, ldb)
 
 
 def load_tune_table(path: str):

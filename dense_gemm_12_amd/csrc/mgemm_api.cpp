@@ -543,6 +543,27 @@ size_t mg_workspace_size(mg_dtype in_type, mg_dtype c_type, mg_op ta, mg_op tb, 
   return packed + (sp > 1 ? (size_t)sp * (size_t)M * (size_t)N * 4 : 0);
 }
 
+int mg_chosen_config_ws(mg_dtype in_type, mg_dtype c_type, mg_op ta, mg_op tb, int64_t M, int64_t N,
+                        int64_t K, int64_t lda, int64_t ldb) {
+  if (M <= 0 || N <= 0 || K <= 0) return -1;
+  if ((int)in_type < MG_F32 || (int)in_type > MG_BF16) return -1;
+  Problem p{(int)in_type, (int)c_type, (int)ta, (int)tb, M, N, K, lda, ldb, N, 1.0f, 0.0f,
+            (const void *)(uintptr_t)4096, (const void *)(uintptr_t)4096, nullptr};
+  p.ws_path = true;
+  for (int side = 0; side < 2; ++side) {
+    const Pack k = pack_shape(p, side == 0);
+    if (k.bytes == 0) continue;
+    if (side == 0) {
+      p.lda = k.pitch;
+      p.a_padded = true;
+    } else {
+      p.ldb = k.pitch;
+      p.b_padded = true;
+    }
+  }
+  return plan(p).config;
+}
+
 int mg_num_configs(mg_dtype in_type) {
   int n = 0;
   entries((int)in_type, &n);

@@ -185,6 +185,12 @@ const char *mg_config_name(mg_dtype in_type, int config);
 int mg_chosen_config(mg_dtype in_type, mg_dtype c_type, mg_op ta, mg_op tb, int64_t M, int64_t N,
                      int64_t K);
 
+/* The configuration gemm_ex with a large enough workspace picks (after any
+ * operand repacking), for 16-byte-aligned base pointers with these leading
+ * dimensions; -1 if none fits. */
+int mg_chosen_config_ws(mg_dtype in_type, mg_dtype c_type, mg_op ta, mg_op tb, int64_t M, int64_t N,
+                        int64_t K, int64_t lda, int64_t ldb);
+
 /* Load a shape-keyed tuning table (text, one rule per line:
  * "<in> <c> <ta> <tb> <M> <N> <K> <config-name> [ws]", e.g. "f16 f16 N T 4096 4096 4096
  * dma_f16_256x256x64_s2_w2x4"); lines starting with '#' are comments.  A rule

@@ -217,6 +217,8 @@ def test_workspace_size_matches_the_split_rule(mg):
     w = lib.mg_workspace_size(mg.MG_BF16, mg.MG_F32, 0, 0, M, N, K, 4095, 4096)
     packed = M * 4096 * 2
     assert w >= packed + 2 * M * N * 4 and (w - packed) % (M * N * 4) == 0
+    cfg = lib.mg_chosen_config_ws(mg.MG_BF16, mg.MG_F32, 0, 0, M, N, K, 4095, 4096)
+    assert cfg >= 0 and not mg.config_name("bf16", cfg).startswith("elem")  # A is repacked
     w2 = lib.mg_workspace_size(mg.MG_BF16, mg.MG_F32, 0, 0, M, N, 4096, 4096, 4096)
     assert w2 % (M * N * 4) == 0 and w2 >= 2 * M * N * 4
     assert lib.mg_workspace_size(mg.MG_F16, mg.MG_F16, 0, 1, 4096, 4096, 4096, 4096, 4096) == 0
