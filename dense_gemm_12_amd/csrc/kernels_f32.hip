@@ -1,7 +1,8 @@
 // fp32 SGEMM configurations: v_mfma_f32_16x16x4_f32.  "dma_" tiles stage
 // operands global -> LDS directly (every layout); "mfma_" tiles stage through
 // registers; "elem" variants load element-wise where 16-byte loads are not
-// legal.
+// legal.  "valu_" runs the same problem on v_fma_f32, for comparison (the
+// planner's heuristic never picks it).
 #include "kernels_inst.hpp"
 
 namespace mg {
@@ -14,6 +15,7 @@ const KernelEntry *entries_f32(int *n) {
       make_dma_entry<float, float, 128, 256, 32, 2, 2, 2>("dma_f32_128x256x32_s2_w2x2"),
       make_dma_entry<float, float, 128, 128, 32, 2, 2, 2>("dma_f32_128x128x32_s2_w2x2"),
       make_dma_entry<float, float, 128, 128, 16, 4, 2, 2>("dma_f32_128x128x16_s4_w2x2"),
+      make_valu_entry<128, 128, 16>("valu_f32_128x128x16"),
       make_entry<float, float, 128, 128, 32, 2, 2, true, true>("mfma_f32_128x128x32_w2x2"),
       make_entry<float, float, 256, 128, 32, 2, 2, true, true>("mfma_f32_256x128x32_w2x2"),
       make_entry<float, float, 128, 256, 32, 2, 2, true, true>("mfma_f32_128x256x32_w2x2"),

@@ -3,6 +3,7 @@
 #pragma once
 #include "gemm_dma_kernel.hpp"
 #include "gemm_kernel.hpp"
+#include "gemm_valu_kernel.hpp"
 
 namespace mg {
 
@@ -76,6 +77,33 @@ KernelEntry make_dma_entry(const char *name) {
   e.kind = 1;
   DmaLayoutSet<TI, float, BM, BN, BK, ST, WM, WN>::fill(e.fn[1]);
   DmaLayoutSet<TI, TO16, BM, BN, BK, ST, WM, WN>::fill(e.fn[0]);
+  return e;
+}
+
+template <class Tile>
+hipError_t launch_valu_tile(const GemmParams &p, hipStream_t s) {
+  hipLaunchKernelGGL(gemm_valu_kernel<Tile>, dim3(p.tiles_m * p.tiles_n * p.splits), dim3(Tile::NT), 0, s,
+                     p);
+  return hipGetLastError();
+}
+
+// fp32 on the vector ALUs (kind 2): every layout, fp32 C only.
+template <int BM, int BN, int BK>
+KernelEntry make_valu_entry(const char *name) {
+  KernelEntry e{};
+  e.name = name;
+  e.bm = BM;
+  e.bn = BN;
+  e.bk = BK;
+  e.a_vec = true;
+  e.b_vec = true;
+  e.kind = 2;
+  for (int c = 0; c < 2; ++c) {
+    e.fn[c][0][0] = &launch_valu_tile<ValuTile<BM, BN, BK, false, false>>;
+    e.fn[c][0][1] = &launch_valu_tile<ValuTile<BM, BN, BK, false, true>>;
+    e.fn[c][1][0] = &launch_valu_tile<ValuTile<BM, BN, BK, true, false>>;
+    e.fn[c][1][1] = &launch_valu_tile<ValuTile<BM, BN, BK, true, true>>;
+  }
   return e;
 }
 

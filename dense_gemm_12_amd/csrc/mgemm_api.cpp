@@ -143,7 +143,8 @@ int64_t tiles_for(int64_t M, int64_t N, int bm, int bn) {
 // Built-in choice among the fully vectorised configurations that support the
 // problem's layout: the largest tile that still gives at least one workgroup
 // per CU (256 CUs), else the tile with the most workgroups; direct-to-LDS
-// kernels win ties, then table order.
+// kernels win ties, then table order.  The vector-ALU tiles (kind 2) run only
+// when forced or named by the tuning table.
 int heuristic_config(const Problem &p) {
   int n = 0;
   const KernelEntry *e = entries(p.in_type, &n);
@@ -151,7 +152,7 @@ int heuristic_config(const Problem &p) {
   int best = -1;
   int64_t bk0 = 0, bk1 = 0, bk2 = 0, bk3 = 0;
   for (int i = 0; i < n; ++i) {
-    if (!e[i].a_vec || !e[i].b_vec || e[i].fn[c][akc][bkc] == nullptr) continue;
+    if (!e[i].a_vec || !e[i].b_vec || e[i].fn[c][akc][bkc] == nullptr || e[i].kind == 2) continue;
     const int64_t t = tiles_for(p.M, p.N, e[i].bm, e[i].bn);
     const int64_t area = (int64_t)e[i].bm * e[i].bn;
     const int64_t k0 = t >= 256, k1 = t >= 256 ? area : t, k2 = t >= 256 ? e[i].kind : area,
