@@ -10,13 +10,14 @@ Each configuration gets a warm-up, then ``--trials`` timed runs of enough
 launches to pass ``--min-ms``, timed with HIP events on the launch stream;
 the median trial decides.  Table rows are
 
-    <in> <c> <ta> <tb> <M> <N> <K> <config> [ws]
+    <in> <c> <ta> <tb> <M> <N> <K> <config> [ws [s=<splits>]]
 
 and the library matches a problem to the nearest row of the same type and
 layout class (log-distance in M, N, K).  Rows tagged ``ws`` were tuned
 through gemm_ex with a workspace (split-K and operand repacking allowed) and
 apply only to such calls; a workload gets one when the planner would split
-or repack it.  The per-configuration timings are
+or repack it, and its split count is tuned too (``s=N``; without it the
+planner's fill rule decides).  The per-configuration timings are
 kept as comments.
 """
 from __future__ import annotations
@@ -32,10 +33,14 @@ ROOT = os.path.dirname(HERE)
 sys.path.insert(0, ROOT)
 
 
-def time_config(mg, torch, A, B, C, w, cfg, trials, min_ms, workspace=None):
+SPLIT_CHOICES = (0, 4, 8, 16, 32)  # workspace pass: the planner's fill rule, then fixed counts
+
+
+def time_config(mg, torch, A, B, C, w, cfg, trials, min_ms, workspace=None, splits=0):
     stream = torch.cuda.current_stream()
     call = lambda: mg.gemm(A, B, C, alpha=w["alpha"], beta=w["beta"], trans_a=w["ta"],
-                           trans_b=w["tb"], config=cfg, stream=stream, workspace=workspace)
+                           trans_b=w["tb"], config=cfg, stream=stream, workspace=workspace,
+                           splits=splits)
     call()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -66,7 +71,7 @@ def tune(names, out, trials=3, min_ms=20.0, log=print):
     mg.load()
     dev = torch.device("cuda:0")
     lines = ["# dense_gemm_12_amd tuning table for gfx950 (MI355X); written by autotune.py",
-             "# <in> <c> <ta> <tb> <M> <N> <K> <config> [ws]; comments: the three fastest candidates"]
+             "# <in> <c> <ta> <tb> <M> <N> <K> <config> [ws [s=N]]; comments: the three fastest candidates"]
     for name in names:
         w = gi.WORKLOADS[name]
         A, B, C = gi.workload_inputs(name)
@@ -78,29 +83,41 @@ def tune(names, out, trials=3, min_ms=20.0, log=print):
                                 w["M"], w["N"], w["K"], Ad.stride(0), Bd.stride(0))
         # plain calls, then (when gemm_ex would split or repack) calls with a
         # workspace, each tuned into its own rule
-        passes = [("", None)]
+        passes = [("", None, (0,))]
         if wsb:
-            passes.append((" ws", torch.empty(wsb, dtype=torch.uint8, device=dev)))
-        for tag, ws in passes:
+            # room for the operand copies and the largest split count tried
+            big = wsb + max(SPLIT_CHOICES) * w["M"] * w["N"] * 4
+            passes.append((" ws", torch.empty(big, dtype=torch.uint8, device=dev), SPLIT_CHOICES))
+        for tag, ws, split_choices in passes:
             results = []
             for cfg in range(mg.num_configs(w["in_dtype"])):
                 cname = mg.config_name(w["in_dtype"], cfg)
-                try:
-                    ms = time_config(mg, torch, Ad, Bd, Cd, w, cfg, trials, min_ms, workspace=ws)
-                except mg.MgemmError as e:
-                    if e.status != mg.MG_EUNSUPPORTED:
-                        raise
-                    continue
-                flops = 2.0 * w["M"] * w["N"] * w["K"]
-                results.append((ms, cname))
-                log(f"{name + tag:28s} {cname:32s} {ms * 1e3:10.1f} us {flops / ms / 1e9:9.1f} TFLOPS")
+                for sp in split_choices:
+                    try:
+                        ms = time_config(mg, torch, Ad, Bd, Cd, w, cfg, trials, min_ms, workspace=ws,
+                                         splits=sp)
+                    except mg.MgemmError as e:
+                        if e.status != mg.MG_EUNSUPPORTED:
+                            raise
+                        break
+                    flops = 2.0 * w["M"] * w["N"] * w["K"]
+                    label = cname + (f" s={sp}" if sp else "")
+                    results.append((ms, cname, sp))
+                    log(f"{name + tag:28s} {label:38s} {ms * 1e3:10.1f} us {flops / ms / 1e9:9.1f} TFLOPS")
             if not results:
                 continue
             results.sort()
-            best = results[0][1]
-            lines.append(f"# {name}{tag}: " + ", ".join(f"{c}={ms * 1e3:.1f}us" for ms, c in results[:3]))
+            best_ms, best, best_sp = results[0]
+            if best_sp:
+                # a fixed split count must beat the fill rule by more than noise
+                auto = [ms for ms, c, sp in results if c == best and sp == 0]
+                if auto and auto[0] <= best_ms * 1.02:
+                    best_sp = 0
+            rule_tag = tag + (f" s={best_sp}" if best_sp else "")
+            lines.append(f"# {name}{tag}: " + ", ".join(
+                f"{c}{'/s=%d' % sp if sp else ''}={ms * 1e3:.1f}us" for ms, c, sp in results[:3]))
             lines.append(f"{w['in_dtype']} {w['c_dtype']} {'T' if w['ta'] else 'N'} {'T' if w['tb'] else 'N'} "
-                         f"{w['M']} {w['N']} {w['K']} {best}{tag}")
+                         f"{w['M']} {w['N']} {w['K']} {best}{rule_tag}")
         del Ad, Bd, Cd
         torch.cuda.empty_cache()
     tmp = out + ".tmp"

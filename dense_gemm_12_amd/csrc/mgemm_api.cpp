@@ -43,7 +43,8 @@ struct Rule {
   int in, c, ta, tb;
   int64_t M, N, K;
   std::string config;
-  bool ws;  // tuned for the workspace path (split-K and operand repacking allowed)
+  bool ws;     // tuned for the workspace path (split-K and operand repacking allowed)
+  int splits;  // ws rules: the tuned split count (0: the planner's fill rule)
 };
 std::vector<Rule> g_rules;  // read-only after mg_load_tune_table
 
@@ -134,6 +135,7 @@ bool b_vec_ok(const Problem &p) {
 struct Plan {
   int config;
   bool a_vec, b_vec;
+  int splits;  // split count a workspace-path rule asks for (0: none)
 };
 
 int64_t tiles_for(int64_t M, int64_t N, int bm, int bn) {
@@ -166,7 +168,7 @@ int heuristic_config(const Problem &p) {
   return best;
 }
 
-int table_config(const Problem &p, bool ws_rules) {
+int table_config(const Problem &p, bool ws_rules, int *splits = nullptr) {
   const Rule *best = nullptr;
   double best_d = 1e300;
   for (const Rule &r : g_rules) {
@@ -180,6 +182,7 @@ int table_config(const Problem &p, bool ws_rules) {
     }
   }
   if (!best || best_d > 1.5) return -1;  // only near neighbours are trusted
+  if (splits) *splits = best->splits;
   return find_config(p.in_type, best->config.c_str());
 }
 
@@ -197,9 +200,13 @@ Plan plan(const Problem &p) {
   Plan pl;
   pl.a_vec = a_vec_ok(p);
   pl.b_vec = b_vec_ok(p);
+  pl.splits = 0;
   if (pl.a_vec && pl.b_vec) {
-    int c = p.ws_path ? table_config(p, true) : -1;
-    if (c < 0) c = table_config(p, false);
+    int c = p.ws_path ? table_config(p, true, &pl.splits) : -1;
+    if (c < 0) {
+      pl.splits = 0;
+      c = table_config(p, false);
+    }
     if (c >= 0) {
       // a rule naming an element-load variant was tuned on operands 16-byte
       // loads could not read; these can be, so the rule does not apply
@@ -234,10 +241,10 @@ static int split_shape(int64_t K, int bk, int s, int *chunk) {
 // The planner's split count: 1 unless the tile grid leaves CUs idle; then
 // enough ranges to give every CU a workgroup, each at least two slices
 // deep, and no more than the workspace holds.
-static int auto_splits(const Problem &p, const KernelEntry &k, int64_t ws_bytes) {
+static int auto_splits(const Problem &p, const KernelEntry &k, int64_t ws_bytes, int hint) {
   const int64_t t = tiles_for(p.M, p.N, k.bm, k.bn);
-  if (t >= kFillWorkgroups || p.K <= 0) return 1;
-  int64_t s = (kFillWorkgroups + t - 1) / t;
+  if (p.K <= 0 || (hint == 0 && t >= kFillWorkgroups)) return 1;
+  int64_t s = hint > 0 ? hint : (kFillWorkgroups + t - 1) / t;
   const int64_t by_k = p.K / (2 * (int64_t)k.bk);
   const int64_t by_ws = ws_bytes / (p.M * p.N * 4);
   if (s > by_k) s = by_k;
@@ -361,7 +368,7 @@ static mg_status run(const Problem &p, int forced, int splits, void *ws, size_t 
     gp.tiles_n = (int)((p.N + k.bn - 1) / k.bn);
     gp.group_m = 8;
     int chunk = 0;
-    const int sp = split_shape(p.K, k.bk, splits == 0 ? auto_splits(p, k, (int64_t)ws_bytes) : splits,
+    const int sp = split_shape(p.K, k.bk, splits == 0 ? auto_splits(p, k, (int64_t)ws_bytes, pl.splits) : splits,
                                &chunk);
     if ((int64_t)gp.tiles_m * gp.tiles_n * sp >= kMaxDim) return MG_EUNSUPPORTED;
     gp.splits = sp;
@@ -535,12 +542,12 @@ size_t mg_workspace_size(mg_dtype in_type, mg_dtype c_type, mg_op ta, mg_op tb, 
       p.b_padded = true;
     }
   }
-  const int cfg = plan(p).config;
-  if (cfg < 0) return packed;
+  const Plan pl = plan(p);
+  if (pl.config < 0) return packed;
   int n = 0;
-  const KernelEntry &k = entries(p.in_type, &n)[cfg];
+  const KernelEntry &k = entries(p.in_type, &n)[pl.config];
   int chunk = 0;
-  const int sp = split_shape(K, k.bk, auto_splits(p, k, INT64_MAX), &chunk);
+  const int sp = split_shape(K, k.bk, auto_splits(p, k, INT64_MAX, pl.splits), &chunk);
   return packed + (sp > 1 ? (size_t)sp * (size_t)M * (size_t)N * 4 : 0);
 }
 
@@ -605,11 +612,13 @@ mg_status mg_load_tune_table(const char *path) {
       ok = false;
       break;
     }
-    char in[16], c[16], ta[4], tb[4], cfg[128], tag[8] = {0};
+    char in[16], c[16], ta[4], tb[4], cfg[128], tag[8] = {0}, sp[16] = {0};
     long long M, N, K;
-    const int got = sscanf(line, "%15s %15s %3s %3s %lld %lld %lld %127s %7s", in, c, ta, tb, &M, &N, &K, cfg,
-                           tag);
-    if (got < 8 || (got == 9 && strcmp(tag, "ws") != 0)) {
+    const int got = sscanf(line, "%15s %15s %3s %3s %lld %lld %lld %127s %7s %15s", in, c, ta, tb, &M, &N, &K,
+                           cfg, tag, sp);
+    int rule_splits = 0;
+    if (got < 8 || (got >= 9 && strcmp(tag, "ws") != 0) ||
+        (got == 10 && (sscanf(sp, "s=%d", &rule_splits) != 1 || rule_splits < 1 || rule_splits > kMaxSplits))) {
       ok = false;
       break;
     }
@@ -622,7 +631,8 @@ mg_status mg_load_tune_table(const char *path) {
     r.N = N;
     r.K = K;
     r.config = cfg;
-    r.ws = got == 9;
+    r.ws = got >= 9;
+    r.splits = rule_splits;
     if (r.in < 0 || r.c < 0 || r.ta < 0 || r.tb < 0 || find_config(r.in, cfg) < 0) {
       ok = false;
       break;

@@ -192,11 +192,12 @@ int mg_chosen_config_ws(mg_dtype in_type, mg_dtype c_type, mg_op ta, mg_op tb, i
                         int64_t K, int64_t lda, int64_t ldb);
 
 /* Load a shape-keyed tuning table (text, one rule per line:
- * "<in> <c> <ta> <tb> <M> <N> <K> <config-name> [ws]", e.g. "f16 f16 N T 4096 4096 4096
- * dma_f16_256x256x64_s2_w2x4"); lines starting with '#' are comments.  A rule
- * tagged "ws" applies only to gemm_ex calls with a workspace (it was tuned
- * with split-K and operand repacking available); untagged rules apply to
- * every call.  A problem takes the nearest rule of the same type and layout
+ * "<in> <c> <ta> <tb> <M> <N> <K> <config-name> [ws [s=<splits>]]", e.g.
+ * "f16 f16 N T 4096 4096 4096 dma_f16_256x256x64_s2_w2x4"); lines starting with
+ * '#' are comments.  A rule tagged "ws" applies only to gemm_ex calls with a
+ * workspace (it was tuned with split-K and operand repacking available), and
+ * its "s=" count (1..64) replaces the planner's fill rule when gemm_ex is
+ * called with splits = 0; untagged rules apply to every call.  A problem takes the nearest rule of the same type and layout
  * class by log-distance of M, N, K, if one is near enough; rules naming an
  * element-load variant are skipped for operands 16-byte loads can read.
  * Replaces any table loaded before.  Returns MG_EINVAL if the file cannot be

@@ -158,6 +158,15 @@ def test_tune_table_load_and_reject(mg, tmp_path):
     mg.load_tune_table(str(tagged))
     assert mg.load().mg_tune_table_size() == 2
     assert mg.chosen_config("f16", "f16", 0, 1, 4096, 4096, 4096) == 3
+    withsplit = tmp_path / "wss.txt"
+    withsplit.write_text(f"f16 f16 N T 4096 4096 4096 {other} ws s=16\n")
+    mg.load_tune_table(str(withsplit))
+    assert mg.load().mg_tune_table_size() == 1
+    for bad_split in ("s=0", "s=65", "s=x", "t=4"):
+        f = tmp_path / "bs.txt"
+        f.write_text(f"f16 f16 N T 4096 4096 4096 {other} ws {bad_split}\n")
+        with pytest.raises(mg.MgemmError):
+            mg.load_tune_table(str(f))
     badtag = tmp_path / "badtag.txt"
     badtag.write_text(f"f16 f16 N T 4096 4096 4096 {name} wsx\n")
     with pytest.raises(mg.MgemmError):
