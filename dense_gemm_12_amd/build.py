@@ -29,13 +29,16 @@ COMMON = [
 ]
 
 
-# Per-source flags.  fp32 tiles: keep MFMA accumulators in VGPRs.  In the
-# AGPR form the register allocator gives the last MFMA of each accumulator
-# chain a fresh AGPR tuple and rotates all of them back at the loop edge
-# (hundreds of v_accvgpr moves per K slice); every fp32 tile fits in VGPRs at
-# its occupancy.  The 16-bit tiles with 256 accumulators per lane need AGPRs,
-# so the flag is not global.
-FILE_FLAGS = {"kernels_f32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source flags: keep MFMA accumulators in VGPRs.  In the AGPR form the
+# register allocator gives the last MFMA of each accumulator chain a fresh
+# AGPR tuple and rotates all of them back at the loop edge (hundreds of
+# v_accvgpr moves per K slice).  Every fp32 tile, and every 16-bit tile but
+# the 256 x 256 ones of four waves (256 accumulators per lane, which need
+# AGPRs and whose loops are clean), fits in VGPRs at its occupancy, so the
+# flag is per file.
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+FILE_FLAGS = {"kernels_f32.hip": _VGPR_FORM, "kernels_f16_vgpr.hip": _VGPR_FORM,
+              "kernels_bf16_vgpr.hip": _VGPR_FORM}
 
 
 def sources():

@@ -285,8 +285,8 @@ struct DmaTile {
       u32x4 fa0[MI], fb0[NJ], fa1[MI], fb1[NJ];
       issue(0);
       issue(1);
-      wait_vmcnt<LOADS_PER_SLICE>();
-      __syncthreads();
+      wait_vmcnt<LOADS_PER_SLICE>();  // slice 0 landed; slice 1 stays in flight
+      lds_barrier();
       read_frags(lds, 0, fa0, fb0);
       for (int kt = 0; kt < nk; ++kt) {
         const char *st = lds + (kt & 1) * STAGE_BYTES;
@@ -360,8 +360,12 @@ struct DmaTile {
 #pragma unroll
       for (int s = 0; s < STAGES - 1; ++s) issue(s);
       for (int kt = 0; kt < nk; ++kt) {
+        // Slice kt has landed (this wave's DMA; the barrier covers the other
+        // waves'), and every wave has consumed its reads of slice kt-1, whose
+        // buffer the next issue refills.  lds_barrier, not __syncthreads:
+        // the later slices' DMA stays in flight.
         wait_vmcnt<LOADS_PER_SLICE * (STAGES - 2)>();
-        __syncthreads();
+        lds_barrier();
         issue(kt + STAGES - 1);
         const char *st = lds + (kt % STAGES) * STAGE_BYTES;
         u32x4 fa[2][MI], fb[2][NJ];

@@ -50,6 +50,8 @@ struct KernelEntry {
 const KernelEntry *entries_f32(int *n);
 const KernelEntry *entries_f16(int *n);
 const KernelEntry *entries_bf16(int *n);
+const KernelEntry *entries_f16_vgpr(int *n);   // the configurations compiled with VGPR-form MFMAs
+const KernelEntry *entries_bf16_vgpr(int *n);
 
 LaunchFn scale_launcher(int c_dtype);   // 0 = f32, 1 = f16, 2 = bf16
 LaunchFn reduce_launcher(int c_dtype);  // split-K partial sums -> C, same codes

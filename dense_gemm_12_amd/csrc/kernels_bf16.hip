@@ -1,28 +1,27 @@
-// bf16-input GEMM configurations: v_mfma_f32_16x16x32_bf16, fp32 accumulate,
-// BK = 64 (128-byte LDS rows); output bf16 or fp32.
+// bf16-input GEMM configurations: v_mfma_f32_16x16x32_bf16, fp32 accumulate, output
+// bf16 or fp32.  The 256 x 256 tiles of four waves (256 accumulators per lane,
+// held in AGPRs) are instantiated here; every other configuration comes from
+// kernels_bf16_vgpr.hip.
+#include <vector>
+
 #include "kernels_inst.hpp"
 
 namespace mg {
 
 const KernelEntry *entries_bf16(int *n) {
-  static const KernelEntry table[] = {
-      make_dma_entry<__bf16, __bf16, 256, 256, 64, 2, 2, 4>("dma_bf16_256x256x64_s2_w2x4"),
-      make_dma_entry<__bf16, __bf16, 256, 256, 32, 4, 2, 4>("dma_bf16_256x256x32_s4_w2x4"),
-      make_dma_entry<__bf16, __bf16, 256, 256, 64, 2, 2, 2>("dma_bf16_256x256x64_s2_w2x2"),
-      make_dma_entry<__bf16, __bf16, 256, 128, 64, 2, 2, 2>("dma_bf16_256x128x64_s2_w2x2"),
-      make_dma_entry<__bf16, __bf16, 256, 128, 32, 4, 2, 2>("dma_bf16_256x128x32_s4_w2x2"),
-      make_dma_entry<__bf16, __bf16, 128, 128, 64, 3, 2, 2>("dma_bf16_128x128x64_s3_w2x2"),
-      make_entry<__bf16, __bf16, 256, 256, 64, 2, 2, true, true>("mfma_bf16_256x256x64_w2x2"),
-      make_entry<__bf16, __bf16, 256, 128, 64, 2, 2, true, true>("mfma_bf16_256x128x64_w2x2"),
-      make_entry<__bf16, __bf16, 128, 256, 64, 2, 2, true, true>("mfma_bf16_128x256x64_w2x2"),
-      make_entry<__bf16, __bf16, 128, 128, 64, 2, 2, true, true>("mfma_bf16_128x128x64_w2x2"),
-      make_entry<__bf16, __bf16, 64, 64, 64, 2, 2, true, true>("mfma_bf16_64x64x64_w2x2"),
-      make_entry<__bf16, __bf16, 128, 128, 64, 2, 2, false, true>("elemA_bf16_128x128x64_w2x2"),
-      make_entry<__bf16, __bf16, 128, 128, 64, 2, 2, true, false>("elemB_bf16_128x128x64_w2x2"),
-      make_entry<__bf16, __bf16, 128, 128, 64, 2, 2, false, false>("elemAB_bf16_128x128x64_w2x2"),
-  };
-  *n = (int)(sizeof(table) / sizeof(table[0]));
-  return table;
+  static const std::vector<KernelEntry> table = [] {
+    int m = 0;
+    const KernelEntry *v = entries_bf16_vgpr(&m);
+    std::vector<KernelEntry> t(v, v + m);
+    // positions 2 and 6 keep the configuration ids of a single table
+    t.insert(t.begin() + 2,
+        make_dma_entry<__bf16, __bf16, 256, 256, 64, 2, 2, 2>("dma_bf16_256x256x64_s2_w2x2"));
+    t.insert(t.begin() + 6,
+        make_entry<__bf16, __bf16, 256, 256, 64, 2, 2, true, true>("mfma_bf16_256x256x64_w2x2"));
+    return t;
+  }();
+  *n = (int)table.size();
+  return table.data();
 }
 
 }  // namespace mg
