@@ -63,6 +63,34 @@ def time_config(mg, torch, A, B, C, w, cfg, trials, min_ms, workspace=None, spli
     return statistics.median(times)
 
 
+def _prefer_consistent(lines, picks, log, margin=0.02):
+    """Near-ties: when the runner-up is within `margin` of the winner and is
+    what the nearest tuned shape of the same type and layout chose, take the
+    runner-up, so that one shape class does not flip between configurations
+    on run-to-run noise."""
+    import gemm_inputs as gi
+    import math
+    chosen = {(n, t): r[0][1] for n, t, r in picks}
+    for n, t, ranked in picks:
+        if len(ranked) < 2 or ranked[1][0] > ranked[0][0] * (1 + margin):
+            continue
+        w = gi.WORKLOADS[n]
+        key = (w["in_dtype"], w["c_dtype"], w["ta"], w["tb"])
+        dist = lambda o: sum(abs(math.log2((gi.WORKLOADS[o][d] + 1) / (w[d] + 1))) for d in "MNK")
+        peers = [o for o, ot in chosen if ot == t and o != n and (gi.WORKLOADS[o]["in_dtype"], gi.WORKLOADS[o]["c_dtype"],
+                 gi.WORKLOADS[o]["ta"], gi.WORKLOADS[o]["tb"]) == key]
+        if not peers:
+            continue
+        nearest = min(peers, key=dist)
+        if chosen[(nearest, t)] == ranked[1][1] and ranked[1][2] == ranked[0][2]:
+            old, new = ranked[0][1], ranked[1][1]
+            log(f"{n}{t}: {old} and {new} within {margin:.0%}; taking {new} as {nearest} does")
+            lines = [l.replace(f" {old}", f" {new}", 1) if (not l.startswith("#") and l.split()[4:7] ==
+                     [str(w["M"]), str(w["N"]), str(w["K"])] and ((" ws" in l) == (t == " ws"))) else l
+                     for l in lines]
+    return lines
+
+
 def tune(names, out, trials=3, min_ms=20.0, log=print):
     import torch
     import dense_gemm_12_amd as mg
@@ -70,6 +98,7 @@ def tune(names, out, trials=3, min_ms=20.0, log=print):
     os.environ["MGEMM_NO_TUNE_TABLE"] = "1"  # time configurations, not an older table's picks
     mg.load()
     dev = torch.device("cuda:0")
+    picks = []  # (name, tag, ranked [(ms, config, splits)]) in tuning order
     lines = ["# dense_gemm_12_amd tuning table for gfx950 (MI355X); written by autotune.py",
              "# <in> <c> <ta> <tb> <M> <N> <K> <config> [ws [s=N]]; comments: the three fastest candidates"]
     for name in names:
@@ -107,6 +136,7 @@ def tune(names, out, trials=3, min_ms=20.0, log=print):
             if not results:
                 continue
             results.sort()
+            picks.append((name, tag, results))
             best_ms, best, best_sp = results[0]
             if best_sp:
                 # a fixed split count must beat the fill rule by more than noise
@@ -120,6 +150,7 @@ def tune(names, out, trials=3, min_ms=20.0, log=print):
                          f"{w['M']} {w['N']} {w['K']} {best}{rule_tag}")
         del Ad, Bd, Cd
         torch.cuda.empty_cache()
+    lines = _prefer_consistent(lines, picks, log)
     tmp = out + ".tmp"
     with open(tmp, "w") as f:
         f.write("\n".join(lines) + "\n")
