@@ -7,8 +7,12 @@ problem and writes the fastest into the tuning table the library loads
 Problems are the named workloads (their own seeded inputs: the data moves
 the chip's clock under MFMA load, so tuning on other data would mislead).
 Each configuration gets a warm-up, then ``--trials`` timed runs of enough
-launches to pass ``--min-ms``, timed with HIP events on the launch stream;
-the median trial decides.  Table rows are
+launches to pass ``--min-ms`` (at most 200), each launch timed on its own
+with HIP events on the launch stream right after a 512 MiB buffer is
+overwritten; the median launch decides.  Timing launches back to back
+instead (``--warm``) ranks some tiles well above where they land inside a
+program: the 4-wave 256 x 256 fp16 tile is 12-20% faster when it follows
+itself than after any other kernel, while the 8-wave one does not care.  Table rows are
 
     <in> <c> <ta> <tb> <M> <N> <K> <config> [ws [s=<splits>]]
 
@@ -36,7 +40,16 @@ sys.path.insert(0, ROOT)
 SPLIT_CHOICES = (0, 4, 8, 16, 32)  # workspace pass: the planner's fill rule, then fixed counts
 
 
-def time_config(mg, torch, A, B, C, w, cfg, trials, min_ms, workspace=None, splits=0):
+FLUSH_BYTES = 512 << 20  # above the chip's last-level cache (256 MB)
+MAX_COLD_REPS = 200
+
+
+def time_config(mg, torch, A, B, C, w, cfg, trials, min_ms, workspace=None, splits=0, flush=None):
+    """Median time of one call in ms.  With ``flush`` (a CUDA tensor of at
+    least FLUSH_BYTES), every timed call runs alone between its own events
+    right after the buffer is overwritten, so it starts with cold caches and
+    after another kernel, as a GEMM inside a larger program does; without it,
+    calls run back to back and the per-call average of each trial counts."""
     stream = torch.cuda.current_stream()
     call = lambda: mg.gemm(A, B, C, alpha=w["alpha"], beta=w["beta"], trans_a=w["ta"],
                            trans_b=w["tb"], config=cfg, stream=stream, workspace=workspace,
@@ -53,6 +66,19 @@ def time_config(mg, torch, A, B, C, w, cfg, trials, min_ms, workspace=None, spli
     for _ in range(3):
         call()
     times = []
+    if flush is not None:
+        reps = min(reps, MAX_COLD_REPS)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for _ in range(trials):
+            for a, b in ev:
+                flush.zero_()
+                a.record(stream)
+                call()
+                b.record(stream)
+            torch.cuda.synchronize()
+            times += [a.elapsed_time(b) for a, b in ev]
+        return statistics.median(times)
     for _ in range(trials):
         e0.record(stream)
         for _ in range(reps):
@@ -65,39 +91,45 @@ def time_config(mg, torch, A, B, C, w, cfg, trials, min_ms, workspace=None, spli
 
 def _prefer_consistent(lines, picks, log, margin=0.02):
     """Near-ties: when the runner-up is within `margin` of the winner and is
-    what the nearest tuned shape of the same type and layout chose, take the
+    what the nearest tuned shapes of the same type and layout chose, take the
     runner-up, so that one shape class does not flip between configurations
-    on run-to-run noise."""
+    on run-to-run noise.  Only peers whose own pick was decisive (their
+    runner-up more than `margin` behind) count, and every peer at the nearest
+    distance must agree, so one noisy pick cannot pull its neighbours along."""
     import gemm_inputs as gi
     import math
     chosen = {(n, t): r[0][1] for n, t, r in picks}
+    decisive = {(n, t) for n, t, r in picks if len(r) < 2 or r[1][0] > r[0][0] * (1 + margin)}
     for n, t, ranked in picks:
-        if len(ranked) < 2 or ranked[1][0] > ranked[0][0] * (1 + margin):
+        if (n, t) in decisive:
             continue
         w = gi.WORKLOADS[n]
         key = (w["in_dtype"], w["c_dtype"], w["ta"], w["tb"])
         dist = lambda o: sum(abs(math.log2((gi.WORKLOADS[o][d] + 1) / (w[d] + 1))) for d in "MNK")
-        peers = [o for o, ot in chosen if ot == t and o != n and (gi.WORKLOADS[o]["in_dtype"], gi.WORKLOADS[o]["c_dtype"],
-                 gi.WORKLOADS[o]["ta"], gi.WORKLOADS[o]["tb"]) == key]
+        peers = [o for o, ot in chosen if ot == t and o != n and (o, ot) in decisive and
+                 (gi.WORKLOADS[o]["in_dtype"], gi.WORKLOADS[o]["c_dtype"],
+                  gi.WORKLOADS[o]["ta"], gi.WORKLOADS[o]["tb"]) == key]
         if not peers:
             continue
-        nearest = min(peers, key=dist)
-        if chosen[(nearest, t)] == ranked[1][1] and ranked[1][2] == ranked[0][2]:
+        d0 = min(dist(o) for o in peers)
+        nearest = [o for o in peers if dist(o) == d0]
+        if {chosen[(o, t)] for o in nearest} == {ranked[1][1]} and ranked[1][2] == ranked[0][2]:
             old, new = ranked[0][1], ranked[1][1]
-            log(f"{n}{t}: {old} and {new} within {margin:.0%}; taking {new} as {nearest} does")
+            log(f"{n}{t}: {old} and {new} within {margin:.0%}; taking {new} as {', '.join(nearest)} do")
             lines = [l.replace(f" {old}", f" {new}", 1) if (not l.startswith("#") and l.split()[4:7] ==
                      [str(w["M"]), str(w["N"]), str(w["K"])] and ((" ws" in l) == (t == " ws"))) else l
                      for l in lines]
     return lines
 
 
-def tune(names, out, trials=3, min_ms=20.0, log=print):
+def tune(names, out, trials=3, min_ms=20.0, log=print, cold=True):
     import torch
     import dense_gemm_12_amd as mg
     import gemm_inputs as gi
     os.environ["MGEMM_NO_TUNE_TABLE"] = "1"  # time configurations, not an older table's picks
     mg.load()
     dev = torch.device("cuda:0")
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev) if cold else None
     picks = []  # (name, tag, ranked [(ms, config, splits)]) in tuning order
     lines = ["# dense_gemm_12_amd tuning table for gfx950 (MI355X); written by autotune.py",
              "# <in> <c> <ta> <tb> <M> <N> <K> <config> [ws [s=N]]; comments: the three fastest candidates"]
@@ -124,7 +156,7 @@ def tune(names, out, trials=3, min_ms=20.0, log=print):
                 for sp in split_choices:
                     try:
                         ms = time_config(mg, torch, Ad, Bd, Cd, w, cfg, trials, min_ms, workspace=ws,
-                                         splits=sp)
+                                         splits=sp, flush=flush)
                     except mg.MgemmError as e:
                         if e.status != mg.MG_EUNSUPPORTED:
                             raise
@@ -166,9 +198,11 @@ def main():
     ap.add_argument("--workload", nargs="*", default=list(gi.WORKLOADS))
     ap.add_argument("--trials", type=int, default=3)
     ap.add_argument("--min-ms", type=float, default=20.0)
+    ap.add_argument("--warm", action="store_true",
+                    help="time calls back to back instead of each after a cache scrub")
     a = ap.parse_args()
     t0 = time.time()
-    tune(a.workload, a.out, a.trials, a.min_ms, log=lambda s: print(s, flush=True))
+    tune(a.workload, a.out, a.trials, a.min_ms, log=lambda s: print(s, flush=True), cold=not a.warm)
     print(f"tuning took {time.time() - t0:.1f}s", flush=True)
 
 

@@ -15,6 +15,8 @@ const KernelEntry *entries_f32(int *n) {
       make_dma_entry<float, float, 128, 256, 32, 2, 2, 2>("dma_f32_128x256x32_s2_w2x2"),
       make_dma_entry<float, float, 128, 128, 32, 2, 2, 2>("dma_f32_128x128x32_s2_w2x2"),
       make_dma_entry<float, float, 128, 128, 16, 4, 2, 2>("dma_f32_128x128x16_s4_w2x2"),
+      make_dma_entry<float, float, 128, 128, 16, 2, 2, 2>("dma_f32_128x128x16_s2_w2x2"),
+      make_dma_entry<float, float, 128, 128, 16, 3, 2, 2>("dma_f32_128x128x16_s3_w2x2"),
       make_valu_entry<128, 128, 16>("valu_f32_128x128x16"),
       make_entry<float, float, 128, 128, 32, 2, 2, true, true>("mfma_f32_128x128x32_w2x2"),
       make_entry<float, float, 256, 128, 32, 2, 2, true, true>("mfma_f32_256x128x32_w2x2"),
