@@ -5,7 +5,9 @@ problem and writes the fastest into the tuning table the library loads
     python -m dense_gemm_12_amd.autotune [--out PATH] [--workload NAME ...]
 
 Problems are the named workloads (their own seeded inputs: the data moves
-the chip's clock under MFMA load, so tuning on other data would mislead).
+the chip's clock under MFMA load, so tuning on other data would mislead) and
+the tuning shapes of ``gemm_inputs`` (2048^3 to 8192^3 in every layout and
+output-type class the workloads leave out).
 Each configuration gets a warm-up, then ``--trials`` timed runs of enough
 launches to pass ``--min-ms`` (at most 200), each launch timed on its own
 with HIP events on the launch stream right after a 512 MiB buffer is
@@ -89,6 +91,11 @@ def time_config(mg, torch, A, B, C, w, cfg, trials, min_ms, workspace=None, spli
     return statistics.median(times)
 
 
+def _shapes():
+    import gemm_inputs as gi
+    return {**gi.WORKLOADS, **gi.TUNING_SHAPES}
+
+
 def _prefer_consistent(lines, picks, log, margin=0.02):
     """Near-ties: when the runner-up is within `margin` of the winner and is
     what the nearest tuned shapes of the same type and layout chose, take the
@@ -96,19 +103,18 @@ def _prefer_consistent(lines, picks, log, margin=0.02):
     on run-to-run noise.  Only peers whose own pick was decisive (their
     runner-up more than `margin` behind) count, and every peer at the nearest
     distance must agree, so one noisy pick cannot pull its neighbours along."""
-    import gemm_inputs as gi
     import math
+    shapes = _shapes()
     chosen = {(n, t): r[0][1] for n, t, r in picks}
     decisive = {(n, t) for n, t, r in picks if len(r) < 2 or r[1][0] > r[0][0] * (1 + margin)}
     for n, t, ranked in picks:
         if (n, t) in decisive:
             continue
-        w = gi.WORKLOADS[n]
+        w = shapes[n]
         key = (w["in_dtype"], w["c_dtype"], w["ta"], w["tb"])
-        dist = lambda o: sum(abs(math.log2((gi.WORKLOADS[o][d] + 1) / (w[d] + 1))) for d in "MNK")
+        dist = lambda o: sum(abs(math.log2((shapes[o][d] + 1) / (w[d] + 1))) for d in "MNK")
         peers = [o for o, ot in chosen if ot == t and o != n and (o, ot) in decisive and
-                 (gi.WORKLOADS[o]["in_dtype"], gi.WORKLOADS[o]["c_dtype"],
-                  gi.WORKLOADS[o]["ta"], gi.WORKLOADS[o]["tb"]) == key]
+                 (shapes[o]["in_dtype"], shapes[o]["c_dtype"], shapes[o]["ta"], shapes[o]["tb"]) == key]
         if not peers:
             continue
         d0 = min(dist(o) for o in peers)
@@ -133,8 +139,9 @@ def tune(names, out, trials=3, min_ms=20.0, log=print, cold=True):
     picks = []  # (name, tag, ranked [(ms, config, splits)]) in tuning order
     lines = ["# dense_gemm_12_amd tuning table for gfx950 (MI355X); written by autotune.py",
              "# <in> <c> <ta> <tb> <M> <N> <K> <config> [ws [s=N]]; comments: the three fastest candidates"]
+    shapes = _shapes()
     for name in names:
-        w = gi.WORKLOADS[name]
+        w = shapes[name]
         A, B, C = gi.workload_inputs(name)
         Ad, Bd = A.to(dev), B.to(dev)
         Cd = (C.to(dev) if C is not None else
@@ -195,7 +202,7 @@ def main():
     import gemm_inputs as gi
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", default=os.path.join(HERE, "tune_gfx950.txt"))
-    ap.add_argument("--workload", nargs="*", default=list(gi.WORKLOADS))
+    ap.add_argument("--workload", nargs="*", default=list(gi.WORKLOADS) + list(gi.TUNING_SHAPES))
     ap.add_argument("--trials", type=int, default=3)
     ap.add_argument("--min-ms", type=float, default=20.0)
     ap.add_argument("--warm", action="store_true",

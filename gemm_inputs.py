@@ -89,13 +89,42 @@ WORKLOADS = {
 }
 
 
+
+# ---- tuning shapes ----------------------------------------------------------
+# Square problems (2048^3, 4096^3, 8192^3) for every layout / output-type class that
+# the named workloads leave out, so that the tuning table has a rule for each
+# class: fp32 NT/TN/TT; fp16 with fp16 C in NN/TN/TT; fp16 with fp32 C and
+# bf16 with bf16 C in all four layouts; bf16 with fp32 C in NT/TN/TT.  Inputs
+# as in the named workloads of the same input type (fp32 N(0,1), 16-bit
+# N(0,1)/sqrt(K)); alpha = 1, beta = 0; seeds from workload number 9.  Names
+# carry the operation flags (opNT: ta = N, tb = T, the layout the pages call
+# "TN" and the fp16 workloads use).
+def _tuning_shapes():
+    out = {}
+    covered = {("f32", "f32", False, False), ("f16", "f16", False, True), ("bf16", "f32", False, False)}
+    for ind, cd in (("f32", "f32"), ("f16", "f16"), ("f16", "f32"), ("bf16", "f32"), ("bf16", "bf16")):
+        for ta in (False, True):
+            for tb in (False, True):
+                if (ind, cd, ta, tb) in covered:
+                    continue
+                for n in (2048, 4096, 8192):
+                    name = f"{ind}{'' if cd == ind else '_c' + cd}_op{'NT'[ta]}{'NT'[tb]}_{n}"
+                    out[name] = dict(wid=9, in_dtype=ind, c_dtype=cd, M=n, N=n, K=n, ta=ta, tb=tb,
+                                     alpha=1.0, beta=0.0, dist="normal" if ind == "f32" else "normal_k")
+    return out
+
+
+TUNING_SHAPES = _tuning_shapes()
+
+
 def workload_inputs(name: str, integer_twin: bool = False):
-    """(A, B, C_in) CPU tensors of a named workload; C_in is None when beta == 0.
+    """(A, B, C_in) CPU tensors of a named workload (or tuning shape); C_in is
+    None when beta == 0.
 
     A is stored M x K (K x M if ta), B stored K x N (N x K if tb); C_in is
     M x N in the output dtype.  The integer twin draws every matrix from
     {-2..2} with seeds offset by 100."""
-    w = WORKLOADS[name]
+    w = WORKLOADS[name] if name in WORKLOADS else TUNING_SHAPES[name]
     M, N, K = w["M"], w["N"], w["K"]
     sa = (K, M) if w["ta"] else (M, K)
     sb = (N, K) if w["tb"] else (K, N)

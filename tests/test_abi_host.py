@@ -266,3 +266,23 @@ def test_split16_arguments_are_rejected_before_launch(mg):
     assert s16(mg, M=-1) == E
     assert s16(mg, K=(1 << 22) + 1, ws_bytes=1 << 62) == mg.MG_EUNSUPPORTED
     assert s16(mg, M=0, ws=None, ws_bytes=0) == mg.MG_OK  # empty: nothing to do
+
+
+def test_shipped_table_covers_every_class_and_each_rule_wins_its_own_shape(mg):
+    mg.load_tune_table(mg.TUNE_TABLE)
+    classes = set()
+    for line in open(mg.TUNE_TABLE):
+        if line.startswith("#") or not line.strip():
+            continue
+        f = line.split()
+        if len(f) > 8:  # workspace rules apply only to gemm_ex calls
+            continue
+        ind, cd, ta, tb = f[0], f[1], f[2] == "T", f[3] == "T"
+        M, N, K = map(int, f[4:7])
+        classes.add((ind, cd, ta, tb))
+        got = mg.chosen_config(ind, cd, int(ta), int(tb), M, N, K)
+        assert mg.config_name(ind, got) == f[7], line
+    want = {(i, c, ta, tb) for i, c in (("f32", "f32"), ("f16", "f16"), ("f16", "f32"), ("bf16", "f32"),
+                                        ("bf16", "bf16"))
+            for ta in (False, True) for tb in (False, True)}
+    assert classes == want
