@@ -46,6 +46,28 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
+// ds_read_b64_tr_b16 as inline assembly.  The compiler's builtin for it is
+// treated as possibly reading what any LDS DMA still in flight writes, so a
+// vmcnt(0) wait goes in front of it, which drains every slice of DMA the
+// schedules keep in flight.  The schedules order these reads against the
+// DMA themselves (vmcnt waits and barriers), and since the compiler does
+// not know the result arrives later, they also wait for it explicitly
+// (lgkmcnt(0) followed by a scheduling fence, so that no MFMA is moved
+// above the wait) before any MFMA reads it.
+__device__ __forceinline__ u32x2 ds_read_tr16_b64(const char *p) {
+  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(a));
+  return v;
+}
+
+// Waits for this wave's LDS reads and keeps every later instruction below.
+__device__ __forceinline__ void wait_lgkm0_fenced() {
+  __builtin_amdgcn_sched_barrier(0);
+  wait_lgkm0();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Workgroup barrier for LDS hand-offs whose completion the caller has
 // already established with explicit vmcnt/lgkmcnt waits.  Unlike
 // __syncthreads() it carries no memory fence, so DMA issued for later slices
@@ -152,10 +174,7 @@ struct DmaOperand {
       if constexpr (KC) {
         f = *reinterpret_cast<const u32x4 *>(st + base + b * 16 * ROWB + xo[ks]);
       } else if constexpr (TR16) {
-        const char *pa = st + base + (ks * 32 + 4 * h) * ROWB + xo[b];
-        const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4 *)((__attribute__((address_space(3))) char *)pa));
-        const u32x2 w = __builtin_bit_cast(u32x2, v);
+        const u32x2 w = ds_read_tr16_b64(st + base + (ks * 32 + 4 * h) * ROWB + xo[b]);
         if (h == 0) {
           f.x = w.x;
           f.y = w.y;
@@ -171,7 +190,7 @@ struct DmaOperand {
 };
 
 template <typename TI, typename TO, int BM_, int BN_, int BK_, int STAGES_, int WAVES_M, int WAVES_N,
-          bool A_KC, bool B_KC>
+          bool A_KC, bool B_KC, bool PINGPONG = false>
 struct DmaTile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
   static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
@@ -192,6 +211,9 @@ struct DmaTile {
   static constexpr int MFMAS = MI * NJ * SUB;
   // fp32 k-major operands order the rows of each 64-row quad as 4j + t.
   static constexpr bool A_Q = ES == 4 && !A_KC, B_Q = ES == 4 && !B_KC;
+  // k-major 16-bit fragments come from ds_read_tr16_b64, whose results the
+  // schedules wait for explicitly.
+  static constexpr bool ASM_READS = ES == 2 && (!A_KC || !B_KC);
   static_assert(KSTEPS == 1 || KSTEPS == 2, "one or two k-steps per slice");
   static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS budget");
   static_assert(LOADS_PER_SLICE * (STAGES - 1) < 64, "vmcnt range");
@@ -267,7 +289,63 @@ struct DmaTile {
       for (int t = 0; t < MFMAS; ++t) mfma(t, fa, fb);
     };
 
-    if constexpr (STAGES == 2 && KSTEPS == 2) {
+    if constexpr (PINGPONG) {
+      // Ping-pong schedule, gfx950's form of the pages' producer/consumer
+      // split ("Warp Specialization HGEMM": copy warps feed compute warps
+      // through a ring).  The eight waves form two groups of four, one wave
+      // of each group per SIMD (waves w and w + 4 share SIMD w), and every
+      // wave alternates between a memory phase and a compute phase:
+      //   memory phase of slice i: issue this wave's share of the DMA for
+      //     slice i + STAGES - 1 (into the buffer of slice i - 1), then read
+      //     its slice-i fragments from LDS into registers;
+      //   compute phase of slice i: the slice's MFMAs, nothing else.
+      // Group 1 starts one phase late, so on each SIMD one wave issues MFMAs
+      // back to back while its partner issues the memory instructions, and
+      // no MFMA waits behind a DMA that cannot issue yet.  A barrier ends
+      // every phase (each wave first waits until all but its STAGES - 2
+      // newest slices of DMA have landed):
+      //   - slice i is read by group 0 in phase 2i and by group 1 in phase
+      //     2i + 1, so its buffer is free from phase 2i + 2 on, when the
+      //     memory phase of slice i + 1 refills it;
+      //   - a wave's share of slice i + STAGES - 1 goes out in phase 2i or
+      //     2i + 1 and is read from phase 2i + 2 STAGES - 2 on.
+      // Both groups pass 2 nk barriers (group 1's first phase is idle and its
+      // last compute phase ends without one).
+      static_assert(NW == 8 && KSTEPS == 1 && STAGES >= 3, "ping-pong: 8 waves, one-k-step slices, >= 3 stages");
+      const int grp = wave >> 2;
+      u32x4 fa[MI], fb[NJ];
+#pragma unroll
+      for (int s = 0; s < STAGES - 1; ++s) issue(s);
+      wait_vmcnt<LOADS_PER_SLICE * (STAGES - 2)>();
+      lds_barrier();
+      auto memory_phase = [&](int i) {
+#pragma unroll
+        for (int u = 0; u < LOADS_PER_SLICE; ++u) dma_op(i + STAGES - 1, u);
+        read_frags(lds + (i % STAGES) * STAGE_BYTES, 0, fa, fb);
+        wait_lgkm0();
+      };
+      auto end_phase = [&]() {
+        __builtin_amdgcn_sched_barrier(0);  // the phase's MFMAs stay before its barrier
+        wait_vmcnt<LOADS_PER_SLICE * (STAGES - 2)>();
+        lds_barrier();
+      };
+      if (grp == 0) {
+        for (int i = 0; i < nk; ++i) {
+          memory_phase(i);
+          end_phase();
+          mfmas(fa, fb);
+          end_phase();
+        }
+      } else {
+        end_phase();
+        for (int i = 0; i < nk; ++i) {
+          memory_phase(i);
+          end_phase();
+          mfmas(fa, fb);
+          if (i + 1 < nk) end_phase();
+        }
+      }
+    } else if constexpr (STAGES == 2 && KSTEPS == 2) {
       // Mid-slice barrier schedule.  Per slice kt (buffer S = kt % 2):
       //   phase A: MFMAs of k-step 0, each followed by at most one LDS read
       //            of the k-step 1 fragments of slice kt;
@@ -291,6 +369,7 @@ struct DmaTile {
       for (int kt = 0; kt < nk; ++kt) {
         const char *st = lds + (kt & 1) * STAGE_BYTES;
         const char *nx = lds + ((kt + 1) & 1) * STAGE_BYTES;
+        if constexpr (ASM_READS) wait_lgkm0_fenced();  // fa0 / fb0 (prologue or last phase C)
 #pragma unroll
         for (int t = 0; t < SLOTS; ++t) {  // phase A
           mfma(t, fa0, fb0);
@@ -300,7 +379,7 @@ struct DmaTile {
           __builtin_amdgcn_sched_barrier(0);
         }
         wait_vmcnt<0>();
-        wait_lgkm0();  // this wave's reads of S are done
+        wait_lgkm0_fenced();  // this wave's reads of S are done (phase C's fragments included)
         __syncthreads();
 #pragma unroll
         for (int t = 0; t < SLOTS; ++t) {  // phase C
@@ -372,6 +451,7 @@ struct DmaTile {
         read_frags(st, 0, fa[0], fb[0]);
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
+          if constexpr (ASM_READS) wait_lgkm0_fenced();  // k-step ks's fragments, nothing newer yet
           if (ks + 1 < KSTEPS) read_frags(st, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
           mfmas(fa[ks & 1], fb[ks & 1]);
         }

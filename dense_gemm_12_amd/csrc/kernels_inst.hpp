@@ -52,10 +52,10 @@ hipError_t launch_dma_tile(const GemmParams &p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename TI, typename TO, int BM, int BN, int BK, int ST, int WM, int WN>
+template <typename TI, typename TO, int BM, int BN, int BK, int ST, int WM, int WN, bool PP>
 struct DmaLayoutSet {
   template <bool AKC, bool BKC>
-  using T = DmaTile<TI, TO, BM, BN, BK, ST, WM, WN, AKC, BKC>;
+  using T = DmaTile<TI, TO, BM, BN, BK, ST, WM, WN, AKC, BKC, PP>;
   static void fill(LaunchFn (&f)[2][2]) {
     f[0][0] = &launch_dma_tile<T<false, false>>;
     f[0][1] = &launch_dma_tile<T<false, true>>;
@@ -65,7 +65,7 @@ struct DmaLayoutSet {
 };
 
 // Direct-to-LDS configurations (16-bit inputs, 16-byte-loadable operands).
-template <typename TI, typename TO16, int BM, int BN, int BK, int ST, int WM, int WN>
+template <typename TI, typename TO16, int BM, int BN, int BK, int ST, int WM, int WN, bool PP = false>
 KernelEntry make_dma_entry(const char *name) {
   KernelEntry e{};
   e.name = name;
@@ -75,8 +75,8 @@ KernelEntry make_dma_entry(const char *name) {
   e.a_vec = true;
   e.b_vec = true;
   e.kind = 1;
-  DmaLayoutSet<TI, float, BM, BN, BK, ST, WM, WN>::fill(e.fn[1]);
-  DmaLayoutSet<TI, TO16, BM, BN, BK, ST, WM, WN>::fill(e.fn[0]);
+  DmaLayoutSet<TI, float, BM, BN, BK, ST, WM, WN, PP>::fill(e.fn[1]);
+  DmaLayoutSet<TI, TO16, BM, BN, BK, ST, WM, WN, PP>::fill(e.fn[0]);
   return e;
 }
 
