@@ -310,7 +310,7 @@ struct DmaTile {
       //   - a wave's share of slice i + STAGES - 1 goes out in phase 2i or
       //     2i + 1 and is read from phase 2i + 2 STAGES - 2 on.
       // Both groups pass 2 nk barriers (group 1's first phase is idle and its
-      // last compute phase ends without one).
+      // last compute phase ends without one), so the counts match for any nk.
       static_assert(NW == 8 && KSTEPS == 1 && STAGES >= 3, "ping-pong: 8 waves, one-k-step slices, >= 3 stages");
       const int grp = wave >> 2;
       u32x4 fa[MI], fb[NJ];
@@ -337,7 +337,7 @@ struct DmaTile {
           end_phase();
         }
       } else {
-        end_phase();
+        if (nk > 0) end_phase();  // (nk is uniform: with no slices neither group passes a barrier)
         for (int i = 0; i < nk; ++i) {
           memory_phase(i);
           end_phase();

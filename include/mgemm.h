@@ -177,7 +177,15 @@ mg_status gemm_f32_split16(mg_op ta, mg_op tb, int64_t M, int64_t N, int64_t K, 
 size_t mg_split16_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /* Kernel configurations available for an input type, and their names
- * (static strings, e.g. "mfma_256x256x64_w2x2"). */
+ * (static strings).  A name reads
+ * <staging>_<type>_<BM>x<BN>x<BK>[_s<stages>][_w<waves along M>x<waves along N>][_pp],
+ * e.g. "dma_f16_256x256x64_s2_w2x4":
+ *   dma     direct-to-LDS loads (both operands must be 16-byte loadable);
+ *   mfma    16-byte loads staged through registers (same requirement);
+ *   elemA / elemB / elemAB   element loads for A / B / both (any alignment);
+ *   valu    fp32 on the vector ALUs (fp32 C only);
+ *   _pp     the ping-pong schedule (two wave groups alternating between
+ *           matrix instructions and memory instructions). */
 int mg_num_configs(mg_dtype in_type);
 const char *mg_config_name(mg_dtype in_type, int config);
 
