@@ -74,24 +74,31 @@ __global__ void __launch_bounds__(kThreads) colmax_partial(const float *X, int64
   const int r = blockIdx.x * kThreads + threadIdx.x;
   if (r >= R) return;
   const int k0 = blockIdx.y * kchunk, k1 = min(K, k0 + kchunk);
-  float m0 = 0.0f, m1 = 0.0f, m2 = 0.0f, m3 = 0.0f;
+  float m[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   int k = k0;
-  for (; k + 3 < k1; k += 4) {  // four independent loads in flight
-    m0 = fmaxf(m0, fabsf(X[(int64_t)k * ld + r]));
-    m1 = fmaxf(m1, fabsf(X[(int64_t)(k + 1) * ld + r]));
-    m2 = fmaxf(m2, fabsf(X[(int64_t)(k + 2) * ld + r]));
-    m3 = fmaxf(m3, fabsf(X[(int64_t)(k + 3) * ld + r]));
+  for (; k + 7 < k1; k += 8) {  // eight independent loads in flight
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m[u] = fmaxf(m[u], fabsf(X[(int64_t)(k + u) * ld + r]));
   }
-  for (; k < k1; ++k) m0 = fmaxf(m0, fabsf(X[(int64_t)k * ld + r]));
-  pm[(int64_t)blockIdx.y * R + r] = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+  for (; k < k1; ++k) m[0] = fmaxf(m[0], fabsf(X[(int64_t)k * ld + r]));
+#pragma unroll
+  for (int u = 1; u < 8; ++u) m[0] = fmaxf(m[0], m[u]);
+  pm[(int64_t)blockIdx.y * R + r] = m[0];
 }
 
 __global__ void __launch_bounds__(kThreads) colmax_final(const float *pm, int R, int parts, int *exp_out) {
   const int r = blockIdx.x * kThreads + threadIdx.x;
   if (r >= R) return;
-  float m = 0.0f;
-  for (int s = 0; s < parts; ++s) m = fmaxf(m, pm[(int64_t)s * R + r]);
-  exp_out[r] = scale_exp(m);
+  float m[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  int s = 0;
+  for (; s + 7 < parts; s += 8) {  // eight independent loads in flight
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m[u] = fmaxf(m[u], pm[(int64_t)(s + u) * R + r]);
+  }
+  for (; s < parts; ++s) m[0] = fmaxf(m[0], pm[(int64_t)s * R + r]);
+#pragma unroll
+  for (int u = 1; u < 8; ++u) m[0] = fmaxf(m[0], m[u]);
+  exp_out[r] = scale_exp(m[0]);
 }
 
 // Writes the three segments of elements (r, k .. k+3) of the split operand
@@ -126,6 +133,54 @@ __global__ void __launch_bounds__(kThreads) split_direct(const float *X, int64_t
 #pragma unroll
   for (int i = 0; i < 4; ++i) v[i] = k + i < K ? ldexpf(row[k + i], e) : 0.0f;
   put4(out, (int64_t)r * 3 * Kp, Kp, k, v, pattern);
+}
+
+// Row-contiguous source with Kp <= kFusedMaxK: one workgroup per row reads
+// the row once into registers (16-byte loads when vec), takes its largest
+// magnitude, and writes the row's exponent and its split (the same values
+// rowmax_direct and split_direct produce, from one read of the row).
+constexpr int kFusedChunks = 16;  // four-element chunks per thread
+constexpr int kFusedMaxK = kFusedChunks * 4 * kThreads;
+
+__global__ void __launch_bounds__(kThreads) split_rows_fused(const float *X, int64_t ld, int K, int Kp, int vec,
+                                                             int *exp_out, uint16_t *out, int pattern) {
+  __shared__ float part[kThreads / 64];
+  const int r = blockIdx.x;
+  const float *row = X + (int64_t)r * ld;
+  float v[kFusedChunks][4];
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kFusedChunks; ++j) {
+    const int k = (j * kThreads + threadIdx.x) * 4;
+    if (vec && k + 3 < K) {
+      const f32x4 x = *reinterpret_cast<const f32x4 *>(row + k);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[j][e] = x[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[j][e] = k + e < K ? row[k + e] : 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(v[j][e]));
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  float t = part[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) t = fmaxf(t, part[w]);
+  const int ex = scale_exp(t);
+  if (threadIdx.x == 0) exp_out[r] = ex;
+#pragma unroll
+  for (int j = 0; j < kFusedChunks; ++j) {
+    const int k = (j * kThreads + threadIdx.x) * 4;
+    if (k < Kp) {
+      float w4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w4[e] = ldexpf(v[j][e], ex);
+      put4(out, (int64_t)r * 3 * Kp, Kp, k, w4, pattern);
+    }
+  }
 }
 
 // Column source (stored K x R): 64 x 64 tiles through LDS so that both the
@@ -181,11 +236,20 @@ hipError_t split16_prepare(const Split16Plan &s, hipStream_t stream) {
                          X, ld, R, s.K, s.Kp, e, out, pattern);
   };
   // op(A) rows are contiguous when A is stored M x K; op(B) columns when B is
-  // stored N x K.
-  exps(s.A, s.lda, s.M, s.a_rows_contiguous, s.row_exp);
-  exps(s.B, s.ldb, s.N, s.b_cols_contiguous, s.col_exp);
-  split(s.A, s.lda, s.M, s.a_rows_contiguous, s.row_exp, s.Ap, 0);
-  split(s.B, s.ldb, s.N, s.b_cols_contiguous, s.col_exp, s.Bp, 1);
+  // stored N x K.  Contiguous rows short enough for one pass take the fused
+  // kernel.
+  auto side = [&](const float *X, int64_t ld, int R, bool contiguous, int *e, uint16_t *out, int pattern) {
+    if (contiguous && s.Kp <= kFusedMaxK) {
+      const int vec = ((uintptr_t)X % 16 == 0 && ld % 4 == 0) ? 1 : 0;
+      hipLaunchKernelGGL(split_rows_fused, dim3(R), dim3(kThreads), 0, stream, X, ld, s.K, s.Kp, vec, e, out,
+                         pattern);
+    } else {
+      exps(X, ld, R, contiguous, e);
+      split(X, ld, R, contiguous, e, out, pattern);
+    }
+  };
+  side(s.A, s.lda, s.M, s.a_rows_contiguous, s.row_exp, s.Ap, 0);
+  side(s.B, s.ldb, s.N, s.b_cols_contiguous, s.col_exp, s.Bp, 1);
   return hipGetLastError();
 }
 

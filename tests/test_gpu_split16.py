@@ -69,6 +69,17 @@ def test_integer_bit_exact_every_layout(ta, tb):
 
 
 @pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_odd_pitch_and_long_rows(ta, tb):
+    """K = 301: rows of contiguous operands are not 16-byte aligned (element
+    loads in the one-pass row kernel).  K = 17000: past what that kernel
+    holds, so contiguous rows take the two-pass path."""
+    for (M, N, K) in ((64, 48, 301), (40, 24, 17000)):
+        A, B, C = make(M, N, K, ta, tb, "int2", 85)
+        check(A, B, C, alpha=1.0, beta=-1.0, ta=ta, tb=tb, exact=True,
+              what=f"int ta={int(ta)} tb={int(tb)} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
 def test_random_within_fp32_bound(ta, tb):
     for (M, N, K), dist in (((200, 136, 300), "uniform"), ((96, 160, 2000), "normal")):
         A, B, C = make(M, N, K, ta, tb, dist, 91)
