@@ -36,6 +36,7 @@ import subprocess
 import json
 import os
 import platform
+import statistics
 import sys
 import time
 
@@ -170,6 +171,65 @@ def read_clocks():
     return out or None
 
 
+def workload_table(mg, torch, dev, names):
+    """Per-launch time of each workload through the planner (through gemm_ex
+    with a workspace where it would split or repack): warm (median of three
+    runs of back-to-back launches) and cold (median launch after a 512 MiB
+    buffer is overwritten)."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    codes = mg.DTYPE_CODES
+    print("| workload | planner's kernel | warm µs | cold µs | TFLOPS (warm) | % of MFMA peak | "
+          "min bytes / warm time |")
+    print("|---|---|---|---|---|---|---|")
+    for name in names:
+        w = gi.WORKLOADS[name]
+        A, B, C = gi.workload_inputs(name)
+        A, B = A.to(dev), B.to(dev)
+        C = (C.to(dev) if C is not None else
+             torch.zeros((w["M"], w["N"]), dtype=gi.DTYPES[w["c_dtype"]], device=dev))
+        key = (w["in_dtype"], w["c_dtype"], int(w["ta"]), int(w["tb"]), w["M"], w["N"], w["K"])
+        wsb = mg.workspace_size(codes[w["in_dtype"]], codes[w["c_dtype"]], *key[2:], A.stride(0), B.stride(0))
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+        cfg = (mg.chosen_config_ws(*key, A.stride(0), B.stride(0)) if ws is not None else mg.chosen_config(*key))
+        kname = f"`{mg.config_name(w['in_dtype'], cfg)}`" + (" (gemm_ex)" if ws is not None else "")
+
+        def call():
+            mg.gemm(A, B, C, alpha=w["alpha"], beta=w["beta"], trans_a=w["ta"], trans_b=w["tb"], workspace=ws)
+
+        call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        torch.cuda.synchronize()
+        reps = max(20, int(100.0 / max(e0.elapsed_time(e1), 1e-3)))
+        trials = []
+        for _ in range(3):
+            e0.record()
+            for _ in range(reps):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            trials.append(e0.elapsed_time(e1) / reps * 1e3)
+        warm = statistics.median(trials)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(min(reps, 40))]
+        for a, b in ev:
+            flush.zero_()
+            a.record()
+            call()
+            b.record()
+        torch.cuda.synchronize()
+        cold = statistics.median(a.elapsed_time(b) for a, b in ev) * 1e3
+        tf = flops(w) / warm / 1e6
+        tbs = min_bytes(w) / warm / 1e6
+        print(f"| {name} | {kname} | {warm:.1f} | {cold:.1f} | {tf:.1f} | {100 * tf / PEAK_TFLOPS[w['in_dtype']]:.1f} % | "
+              f"{tbs:.2f} TB/s ({100 * tbs / 8:.0f} % of 8) |", flush=True)
+        del A, B, C, ws
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,6 +242,9 @@ def main():
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="extra steps with a 512 MiB cache scrub before each launch (0: skip)")
     ap.add_argument("--no-clocks", action="store_true", help="skip the rocm-smi clock reading")
+    ap.add_argument("--table", action="store_true",
+                    help="instead of the step: time every named workload (or --workload) through the "
+                         "planner, warm and after a cache scrub, and print a markdown table")
     ap.add_argument("--split16-steps", type=int, default=10,
                     help="launches of the fp32 part through split fp16 inputs, reported beside the "
                          "step (0: skip)")
@@ -197,6 +260,9 @@ def main():
     import dense_gemm_12_amd as mg
     mg.load()
     dev = torch.device("cuda:0")
+    if args.table:
+        workload_table(mg, torch, dev, tuple(args.workload) if args.workload else tuple(gi.WORKLOADS))
+        return
     names = tuple(args.workload) if args.workload else STEP
 
     parts_host, parts_dev, calls = [], [], []

@@ -311,6 +311,9 @@ struct DmaTile {
       //     2i + 1 and is read from phase 2i + 2 STAGES - 2 on.
       // Both groups pass 2 nk barriers (group 1's first phase is idle and its
       // last compute phase ends without one), so the counts match for any nk.
+      // A wave's fragment registers are rewritten by its next memory phase
+      // only after the phase barrier and the DMA issue (some thirty
+      // instructions), far past the operand reads of its last MFMA.
       static_assert(NW == 8 && KSTEPS == 1 && STAGES >= 3, "ping-pong: 8 waves, one-k-step slices, >= 3 stages");
       const int grp = wave >> 2;
       u32x4 fa[MI], fb[NJ];
