@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <memory>
 #include <string>
 #include <vector>
 
@@ -46,7 +47,12 @@ struct Rule {
   bool ws;     // tuned for the workspace path (split-K and operand repacking allowed)
   int splits;  // ws rules: the tuned split count (0: the planner's fill rule)
 };
-std::vector<Rule> g_rules;  // read-only after mg_load_tune_table
+// The loaded table.  A loader builds a new vector and publishes it with one
+// atomic store; every call plans with the snapshot it loads at its start, so
+// loading a table while other threads run GEMMs is safe.
+std::shared_ptr<const std::vector<Rule>> g_rules = std::make_shared<const std::vector<Rule>>();
+
+std::shared_ptr<const std::vector<Rule>> rules_snapshot() { return std::atomic_load(&g_rules); }
 
 int find_config(int in_type, const char *name) {
   int n = 0;
@@ -171,7 +177,8 @@ int heuristic_config(const Problem &p) {
 int table_config(const Problem &p, bool ws_rules, int *splits = nullptr) {
   const Rule *best = nullptr;
   double best_d = 1e300;
-  for (const Rule &r : g_rules) {
+  const std::shared_ptr<const std::vector<Rule>> rules = rules_snapshot();
+  for (const Rule &r : *rules) {
     if (r.in != p.in_type || r.c != p.c_type || r.ta != p.ta || r.tb != p.tb || r.ws != ws_rules) continue;
     const double d = fabs(log2((double)(p.M + 1) / (r.M + 1))) +
                      fabs(log2((double)(p.N + 1) / (r.N + 1))) +
@@ -641,11 +648,12 @@ mg_status mg_load_tune_table(const char *path) {
   }
   fclose(f);
   if (!ok) return MG_EINVAL;
-  g_rules.swap(rules);
+  std::atomic_store(&g_rules, std::shared_ptr<const std::vector<Rule>>(
+                                 std::make_shared<const std::vector<Rule>>(std::move(rules))));
   return MG_OK;
 }
 
-int mg_tune_table_size(void) { return (int)g_rules.size(); }
+int mg_tune_table_size(void) { return (int)rules_snapshot()->size(); }
 
 const char *mg_status_str(mg_status s) {
   switch (s) {

@@ -43,8 +43,9 @@
  *   MG_EUNSUPPORTED  valid but outside what the kernels address: a dimension
  *                    >= 2^31, or a leading dimension above 2^21 elements.
  *   MG_EHIP          the launch failed; mg_last_hip_error() gives the code.
- * Functions never throw and never print.  Calls are reentrant; the tuning
- * table (mg_load_tune_table) is read-only once loaded.
+ * Functions never throw and never print.  Calls are reentrant and thread
+ * safe; a GEMM call plans with the tuning table loaded when it starts, even
+ * while another thread loads a new one.
  */
 #ifndef MGEMM_H
 #define MGEMM_H
@@ -210,7 +211,8 @@ int mg_chosen_config_ws(mg_dtype in_type, mg_dtype c_type, mg_op ta, mg_op tb, i
  * element-load variant are skipped for operands 16-byte loads can read.
  * Replaces any table loaded before.  Returns MG_EINVAL if the file cannot be
  * read or a line names an unknown config or tag (the previous table is then
- * kept).  Not safe to call concurrently with GEMM calls. */
+ * kept).  The new table is published atomically: calls already planning keep
+ * the table they started with. */
 mg_status mg_load_tune_table(const char *path);
 /* Number of rules in the loaded table (0 if none). */
 int mg_tune_table_size(void);

@@ -286,3 +286,41 @@ def test_shipped_table_covers_every_class_and_each_rule_wins_its_own_shape(mg):
                                         ("bf16", "bf16"))
             for ta in (False, True) for tb in (False, True)}
     assert classes == want
+
+
+def test_tune_table_reload_while_planning(mg, tmp_path):
+    """Tables published while other threads plan: every plan sees one whole
+    table (ctypes drops the GIL during the calls, so the threads overlap)."""
+    import threading
+    a, b = mg.config_name("f16", 0), mg.config_name("f16", 5)
+    ta, tb = tmp_path / "a.txt", tmp_path / "b.txt"
+    ta.write_text(f"f16 f16 N T 4096 4096 4096 {a}\n")
+    tb.write_text(f"f16 f16 N T 4096 4096 4096 {b}\n" + "".join(
+        f"f16 f16 N T {n} {n} {n} {b}\n" for n in range(100, 400)))
+    want = {mg.config_id("f16", a), mg.config_id("f16", b)}
+    stop = threading.Event()
+    seen, bad = set(), []
+
+    def loader(path):
+        while not stop.is_set():
+            mg.load_tune_table(str(path))
+
+    def planner():
+        while not stop.is_set():
+            c = mg.chosen_config("f16", "f16", 0, 1, 4096, 4096, 4096)
+            seen.add(c)
+            if c not in want:
+                bad.append(c)
+
+    threads = [threading.Thread(target=loader, args=(p,)) for p in (ta, tb)]
+    threads += [threading.Thread(target=planner) for _ in range(2)]
+    for t in threads:
+        t.start()
+    import time
+    time.sleep(1.0)
+    stop.set()
+    for t in threads:
+        t.join()
+    mg.load_tune_table(mg.TUNE_TABLE)
+    assert not bad
+    assert seen <= want and seen
