@@ -28,7 +28,7 @@ EXPORTS = (
     "gemm_f32", "gemm_f16", "gemm_bf16", "gemm_f32_cfg", "gemm_f16_cfg", "gemm_bf16_cfg",
     "gemm_ex", "mg_workspace_size", "gemm_f32_split16", "mg_split16_workspace_size", "mg_chosen_config_ws",
     "mg_num_configs", "mg_config_name", "mg_chosen_config", "mg_load_tune_table",
-    "mg_tune_table_size", "mg_status_str", "mg_last_hip_error", "mg_version",
+    "mg_tune_table_size", "mg_config_occupancy", "mg_status_str", "mg_last_hip_error", "mg_version",
 )
 
 
@@ -88,6 +88,8 @@ def load(path: str | None = None):
         lib.mg_load_tune_table.restype = ci
         lib.mg_tune_table_size.argtypes = []
         lib.mg_tune_table_size.restype = ci
+        lib.mg_config_occupancy.argtypes = [ci, ci]
+        lib.mg_config_occupancy.restype = ci
         lib.mg_status_str.argtypes = [ci]
         lib.mg_status_str.restype = cp
         lib.mg_last_hip_error.argtypes = []
@@ -173,6 +175,11 @@ def config_id(in_type: str, name: str) -> int:
         if config_name(in_type, i) == name:
             return i
     raise KeyError(name)
+
+
+def config_occupancy(in_type: str, config: int) -> int:
+    """Workgroups of a configuration per CU on the current device (-1 if unknown)."""
+    return load().mg_config_occupancy(DTYPE_CODES[in_type], config)
 
 
 def chosen_config(in_type, c_type, ta, tb, M, N, K) -> int:

@@ -19,7 +19,11 @@ itself than after any other kernel, while the 8-wave one does not care.  Table r
     <in> <c> <ta> <tb> <M> <N> <K> <config> [ws [s=<splits>]]
 
 and the library matches a problem to the nearest row of the same type and
-layout class (log-distance in M, N, K).  Rows tagged ``ws`` were tuned
+layout class (log-distance in M, N, K).  The table also records, per
+configuration, the best fraction of the type's peak it reached here
+(``rate <in> <config> <fraction>``); the library's cost model uses these to
+rank configurations for shapes no rule is near, and to drop a neighbouring
+shape's rule that it expects to be clearly slower.  Rows tagged ``ws`` were tuned
 through gemm_ex with a workspace (split-K and operand repacking allowed) and
 apply only to such calls; a workload gets one when the planner would split
 or repack it, and its split count is tuned too (``s=N``; without it the
@@ -40,6 +44,7 @@ sys.path.insert(0, ROOT)
 
 
 SPLIT_CHOICES = (0, 4, 8, 16, 32)  # workspace pass: the planner's fill rule, then fixed counts
+PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6}
 
 
 FLUSH_BYTES = 512 << 20  # above the chip's last-level cache (256 MB)
@@ -137,6 +142,7 @@ def tune(names, out, trials=3, min_ms=20.0, log=print, cold=True):
     dev = torch.device("cuda:0")
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev) if cold else None
     picks = []  # (name, tag, ranked [(ms, config, splits)]) in tuning order
+    rates = {}  # (input type, config) -> best fraction of peak over the plain calls
     lines = ["# dense_gemm_12_amd tuning table for gfx950 (MI355X); written by autotune.py",
              "# <in> <c> <ta> <tb> <M> <N> <K> <config> [ws [s=N]]; comments: the three fastest candidates"]
     shapes = _shapes()
@@ -169,6 +175,9 @@ def tune(names, out, trials=3, min_ms=20.0, log=print, cold=True):
                             raise
                         break
                     flops = 2.0 * w["M"] * w["N"] * w["K"]
+                    if not tag:
+                        frac = flops / ms / 1e9 / PEAK_TFLOPS[w["in_dtype"]]
+                        rates[(w["in_dtype"], cname)] = max(frac, rates.get((w["in_dtype"], cname), 0.0))
                     label = cname + (f" s={sp}" if sp else "")
                     results.append((ms, cname, sp))
                     log(f"{name + tag:28s} {label:38s} {ms * 1e3:10.1f} us {flops / ms / 1e9:9.1f} TFLOPS")
@@ -190,6 +199,14 @@ def tune(names, out, trials=3, min_ms=20.0, log=print, cold=True):
         del Ad, Bd, Cd
         torch.cuda.empty_cache()
     lines = _prefer_consistent(lines, picks, log)
+    # the planner's cost model ranks configurations on shapes no rule is near
+    # by these measured rates
+    lines.append("# rate <in> <config> <best fraction of the type's peak over the plain calls above> "
+                 "<workgroups per CU>")
+    for (t, c), f in sorted(rates.items()):
+        occ = mg.config_occupancy(t, mg.config_id(t, c))
+        if f > 0 and occ > 0:
+            lines.append(f"rate {t} {c} {min(f, 1.0):.4f} {occ}")
     tmp = out + ".tmp"
     with open(tmp, "w") as f:
         f.write("\n".join(lines) + "\n")

@@ -39,12 +39,17 @@ typedef hipError_t (*LaunchFn)(const GemmParams &, hipStream_t);
 // configuration.  a_vec / b_vec tell whether the variant needs
 // 16-byte-loadable operands.  kind: 0 = register-staged loads, 1 = direct
 // global->LDS loads.
+typedef int (*OccupancyFn)();  // workgroups per CU of the kernel, -1 when it cannot be asked
+
 struct KernelEntry {
   const char *name;
   int bm, bn, bk;
   bool a_vec, b_vec;
   int kind;
   LaunchFn fn[2][2][2];
+  int threads;          // workgroup size
+  int lds_bytes;        // static LDS per workgroup
+  OccupancyFn occupancy;  // asked of the HIP runtime for one representative layout
 };
 
 const KernelEntry *entries_f32(int *n);

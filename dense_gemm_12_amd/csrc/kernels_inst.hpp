@@ -7,6 +7,21 @@
 
 namespace mg {
 
+// Workgroups of a kernel that fit on one CU at once (registers, LDS and
+// waves together), as the HIP runtime computes it for the current device.
+template <typename Kernel>
+int occupancy_of(Kernel k, int threads) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, threads, 0) != hipSuccess) {
+    (void)hipGetLastError();  // leave no error behind for the caller's next HIP call
+    return -1;
+  }
+  return n;
+}
+template <class Tile> int occupancy_tile() { return occupancy_of(gemm_kernel<Tile>, Tile::NT); }
+template <class Tile> int occupancy_dma_tile() { return occupancy_of(gemm_dma_kernel<Tile>, Tile::NT); }
+template <class Tile> int occupancy_valu_tile() { return occupancy_of(gemm_valu_kernel<Tile>, Tile::NT); }
+
 template <class Tile>
 hipError_t launch_tile(const GemmParams &p, hipStream_t s) {
   hipLaunchKernelGGL(gemm_kernel<Tile>, dim3(p.tiles_m * p.tiles_n * p.splits), dim3(Tile::NT), 0, s, p);
@@ -42,6 +57,10 @@ KernelEntry make_entry(const char *name) {
   } else {
     LayoutSet<TI, TO16, BM, BN, BK, WM, WN, AV, BV>::fill(e.fn[0]);
   }
+  using Rep = typename LayoutSet<TI, float, BM, BN, BK, WM, WN, AV, BV>::template T<true, true>;
+  e.threads = Rep::NT;
+  e.lds_bytes = 2 * Rep::STAGE_BYTES;
+  e.occupancy = &occupancy_tile<Rep>;
   return e;
 }
 
@@ -77,6 +96,10 @@ KernelEntry make_dma_entry(const char *name) {
   e.kind = 1;
   DmaLayoutSet<TI, float, BM, BN, BK, ST, WM, WN, PP>::fill(e.fn[1]);
   DmaLayoutSet<TI, TO16, BM, BN, BK, ST, WM, WN, PP>::fill(e.fn[0]);
+  using Rep = typename DmaLayoutSet<TI, float, BM, BN, BK, ST, WM, WN, PP>::template T<true, true>;
+  e.threads = Rep::NT;
+  e.lds_bytes = ST * Rep::STAGE_BYTES;
+  e.occupancy = &occupancy_dma_tile<Rep>;
   return e;
 }
 
@@ -104,6 +127,10 @@ KernelEntry make_valu_entry(const char *name) {
     e.fn[c][1][0] = &launch_valu_tile<ValuTile<BM, BN, BK, true, false>>;
     e.fn[c][1][1] = &launch_valu_tile<ValuTile<BM, BN, BK, true, true>>;
   }
+  using Rep = ValuTile<BM, BN, BK, true, true>;
+  e.threads = Rep::NT;
+  e.lds_bytes = 2 * Rep::STAGE_BYTES;
+  e.occupancy = &occupancy_valu_tile<Rep>;
   return e;
 }
 

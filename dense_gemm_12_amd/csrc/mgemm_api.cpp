@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <memory>
 #include <string>
 #include <vector>
@@ -47,12 +48,20 @@ struct Rule {
   bool ws;     // tuned for the workspace path (split-K and operand repacking allowed)
   int splits;  // ws rules: the tuned split count (0: the planner's fill rule)
 };
-// The loaded table.  A loader builds a new vector and publishes it with one
+struct Table {
+  std::vector<Rule> rules;
+  // "rate" lines: the fraction of the input type's peak each configuration
+  // reached at full occupancy when the table was tuned, and its workgroups
+  // per CU on that device (index = config id; 0 where the table gives none).
+  std::vector<float> rate[3];
+  std::vector<int> occ[3];
+};
+// The loaded table.  A loader builds a new table and publishes it with one
 // atomic store; every call plans with the snapshot it loads at its start, so
 // loading a table while other threads run GEMMs is safe.
-std::shared_ptr<const std::vector<Rule>> g_rules = std::make_shared<const std::vector<Rule>>();
+std::shared_ptr<const Table> g_table = std::make_shared<const Table>();
 
-std::shared_ptr<const std::vector<Rule>> rules_snapshot() { return std::atomic_load(&g_rules); }
+std::shared_ptr<const Table> table_snapshot() { return std::atomic_load(&g_table); }
 
 int find_config(int in_type, const char *name) {
   int n = 0;
@@ -148,37 +157,88 @@ int64_t tiles_for(int64_t M, int64_t N, int bm, int bn) {
   return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
 }
 
+// ----------------------------------------------------------- cost model --
+// Workgroups of configuration i (input type in) that fit on one CU, asked of
+// the HIP runtime once (-1 without a device).
+int runtime_occupancy(int in, int i, const KernelEntry &k) {
+  static std::atomic<int> cache[3][64];
+  if (i < 64) {
+    const int c = cache[in][i].load(std::memory_order_relaxed);
+    if (c != 0) return c;
+  }
+  const int n = k.occupancy ? k.occupancy() : -1;
+  if (i < 64) cache[in][i].store(n > 0 ? n : -1, std::memory_order_relaxed);
+  return n > 0 ? n : -1;
+}
+
+// The table's figure (measured where it was tuned, so plans do not depend
+// on whether a device is present), else the runtime's, else a rough figure
+// from LDS and wave count.
+int occupancy(const Table &t, int in, int i, const KernelEntry &k) {
+  if (i < (int)t.occ[in].size() && t.occ[in][i] > 0) return t.occ[in][i];
+  int n = runtime_occupancy(in, i, k);
+  if (n <= 0) {
+    const int by_lds = k.lds_bytes > 0 ? (160 * 1024) / k.lds_bytes : 8;
+    const int by_waves = k.threads >= 512 ? 1 : 2;
+    n = by_lds < by_waves ? by_lds : by_waves;
+    if (n < 1) n = 1;
+  }
+  return n;
+}
+
+// Fraction of the type's peak configuration i reaches at full occupancy:
+// the table's measured rate, else a default by kind that favours larger
+// tiles (their data reuse grows with the tile's side).
+double efficiency(const Table &t, int in, int i, const KernelEntry &k) {
+  if (i < (int)t.rate[in].size() && t.rate[in][i] > 0.0f) return t.rate[in][i];
+  const double base = k.kind == 1 ? 0.45 : (k.kind == 0 ? 0.30 : 0.40);
+  return base * sqrt(sqrt((double)k.bm * k.bn / 65536.0));
+}
+
+// Estimated time of configuration i on problem p (units common to one input
+// type): the grid runs in rounds of 256 CUs x occupancy workgroups, and a
+// round takes (occupancy) tile times at the configuration's full-occupancy
+// efficiency.  A partial round is charged as a full one: workgroups that
+// share a CU with fewer others do not speed up in proportion.
+double est_time(const Table &t, const Problem &p, int i, const KernelEntry &k) {
+  const int occ = occupancy(t, p.in_type, i, k);
+  const int64_t tiles = tiles_for(p.M, p.N, k.bm, k.bn);
+  const int64_t slots = 256 * (int64_t)occ;
+  const int64_t rounds = (tiles + slots - 1) / slots;
+  return (double)rounds * occ * (2.0 * k.bm * k.bn * (double)(p.K > 0 ? p.K : 1)) / efficiency(t, p.in_type, i, k);
+}
+
+bool usable(const KernelEntry &k, const Problem &p) {
+  const int c = p.c_type == MG_F32 ? 1 : 0, akc = p.ta == MG_N, bkc = p.tb == MG_T;
+  return k.a_vec && k.b_vec && k.fn[c][akc][bkc] != nullptr;
+}
+
 // Built-in choice among the fully vectorised configurations that support the
-// problem's layout: the largest tile that still gives at least one workgroup
-// per CU (256 CUs), else the tile with the most workgroups; direct-to-LDS
-// kernels win ties, then table order.  The vector-ALU tiles (kind 2) run only
-// when forced or named by the tuning table.
-int heuristic_config(const Problem &p) {
+// problem's layout: the least estimated time, ties to the larger tile, then
+// table order.  The vector-ALU tiles (kind 2) run only when forced or named
+// by the tuning table.
+int model_config(const Table &t, const Problem &p, double *est = nullptr) {
   int n = 0;
   const KernelEntry *e = entries(p.in_type, &n);
-  const int c = p.c_type == MG_F32 ? 1 : 0, akc = p.ta == MG_N, bkc = p.tb == MG_T;
   int best = -1;
-  int64_t bk0 = 0, bk1 = 0, bk2 = 0, bk3 = 0;
+  double best_t = 0.0;
   for (int i = 0; i < n; ++i) {
-    if (!e[i].a_vec || !e[i].b_vec || e[i].fn[c][akc][bkc] == nullptr || e[i].kind == 2) continue;
-    const int64_t t = tiles_for(p.M, p.N, e[i].bm, e[i].bn);
-    const int64_t area = (int64_t)e[i].bm * e[i].bn;
-    const int64_t k0 = t >= 256, k1 = t >= 256 ? area : t, k2 = t >= 256 ? e[i].kind : area,
-                  k3 = t >= 256 ? 0 : e[i].kind;
-    if (best < 0 || k0 > bk0 || (k0 == bk0 && (k1 > bk1 || (k1 == bk1 && (k2 > bk2 ||
-        (k2 == bk2 && k3 > bk3)))))) {
+    if (!usable(e[i], p) || e[i].kind == 2) continue;
+    const double ti = est_time(t, p, i, e[i]);
+    if (best < 0 || ti < best_t * (1.0 - 1e-9) ||
+        (ti <= best_t * (1.0 + 1e-9) && (int64_t)e[i].bm * e[i].bn > (int64_t)e[best].bm * e[best].bn)) {
       best = i;
-      bk0 = k0; bk1 = k1; bk2 = k2; bk3 = k3;
+      best_t = ti;
     }
   }
+  if (est) *est = best_t;
   return best;
 }
 
-int table_config(const Problem &p, bool ws_rules, int *splits = nullptr) {
+int table_config(const Table &t, const Problem &p, bool ws_rules, int *splits = nullptr, double *dist = nullptr) {
   const Rule *best = nullptr;
   double best_d = 1e300;
-  const std::shared_ptr<const std::vector<Rule>> rules = rules_snapshot();
-  for (const Rule &r : *rules) {
+  for (const Rule &r : t.rules) {
     if (r.in != p.in_type || r.c != p.c_type || r.ta != p.ta || r.tb != p.tb || r.ws != ws_rules) continue;
     const double d = fabs(log2((double)(p.M + 1) / (r.M + 1))) +
                      fabs(log2((double)(p.N + 1) / (r.N + 1))) +
@@ -190,6 +250,7 @@ int table_config(const Problem &p, bool ws_rules, int *splits = nullptr) {
   }
   if (!best || best_d > 1.5) return -1;  // only near neighbours are trusted
   if (splits) *splits = best->splits;
+  if (dist) *dist = best_d;
   return find_config(p.in_type, best->config.c_str());
 }
 
@@ -203,27 +264,32 @@ int elem_config(int in_type, bool a_vec, bool b_vec) {
 }
 
 Plan plan(const Problem &p) {
-  const bool a_kc = p.ta == MG_N, b_kc = p.tb == MG_T;
   Plan pl;
   pl.a_vec = a_vec_ok(p);
   pl.b_vec = b_vec_ok(p);
   pl.splits = 0;
   if (pl.a_vec && pl.b_vec) {
-    int c = p.ws_path ? table_config(p, true, &pl.splits) : -1;
+    const std::shared_ptr<const Table> t = table_snapshot();
+    int n = 0;
+    const KernelEntry *e = entries(p.in_type, &n);
+    int c = p.ws_path ? table_config(*t, p, true, &pl.splits) : -1;
+    double dist = 0.0;
     if (c < 0) {
       pl.splits = 0;
-      c = table_config(p, false);
+      c = table_config(*t, p, false, nullptr, &dist);
+      // a rule for a neighbouring shape is kept unless the cost model expects
+      // it to be clearly slower here (e.g. a tile that filled the GPU there
+      // leaves CUs idle here)
+      if (c >= 0 && dist > 0.0 && usable(e[c], p)) {
+        double best_t = 0.0;
+        const int m = model_config(*t, p, &best_t);
+        if (m >= 0 && est_time(*t, p, c, e[c]) > 1.1 * best_t) c = m;
+      }
     }
-    if (c >= 0) {
-      // a rule naming an element-load variant was tuned on operands 16-byte
-      // loads could not read; these can be, so the rule does not apply
-      int n = 0;
-      const KernelEntry *e = entries(p.in_type, &n);
-      if (e[c].fn[p.c_type == MG_F32 ? 1 : 0][a_kc ? 1 : 0][b_kc ? 1 : 0] == nullptr || !e[c].a_vec ||
-          !e[c].b_vec)
-        c = -1;
-    }
-    pl.config = c >= 0 ? c : heuristic_config(p);
+    // a rule naming an element-load variant was tuned on operands 16-byte
+    // loads could not read; these can be, so the rule does not apply
+    if (c >= 0 && !usable(e[c], p)) c = -1;
+    pl.config = c >= 0 ? c : model_config(*t, p);
   } else {
     pl.config = elem_config(p.in_type, pl.a_vec, pl.b_vec);
   }
@@ -606,7 +672,8 @@ mg_status mg_load_tune_table(const char *path) {
   if (!path) return MG_EINVAL;
   FILE *f = fopen(path, "r");
   if (!f) return MG_EINVAL;
-  std::vector<Rule> rules;
+  Table table;
+  std::vector<Rule> &rules = table.rules;
   char line[512];
   bool ok = true;
   bool continuation = false;  // inside a line longer than the buffer
@@ -618,6 +685,24 @@ mg_status mg_load_tune_table(const char *path) {
     if (!whole) {  // a rule never needs this much text
       ok = false;
       break;
+    }
+    if (!strncmp(line, "rate ", 5)) {  // rate <in> <config> <fraction of peak> <workgroups per CU>
+      char in[16], cfg[128];
+      float frac = 0.0f;
+      int occ = 0;
+      const int in_t = sscanf(line, "rate %15s %127s %f %d", in, cfg, &frac, &occ) == 4 ? parse_dtype(in) : -1;
+      const int id = in_t >= 0 ? find_config(in_t, cfg) : -1;
+      if (id < 0 || !(frac > 0.0f && frac <= 1.0f) || occ < 1 || occ > 32) {
+        ok = false;
+        break;
+      }
+      if ((int)table.rate[in_t].size() <= id) {
+        table.rate[in_t].resize(id + 1, 0.0f);
+        table.occ[in_t].resize(id + 1, 0);
+      }
+      table.rate[in_t][id] = frac;
+      table.occ[in_t][id] = occ;
+      continue;
     }
     char in[16], c[16], ta[4], tb[4], cfg[128], tag[8] = {0}, sp[16] = {0};
     long long M, N, K;
@@ -648,12 +733,18 @@ mg_status mg_load_tune_table(const char *path) {
   }
   fclose(f);
   if (!ok) return MG_EINVAL;
-  std::atomic_store(&g_rules, std::shared_ptr<const std::vector<Rule>>(
-                                 std::make_shared<const std::vector<Rule>>(std::move(rules))));
+  std::atomic_store(&g_table, std::shared_ptr<const Table>(std::make_shared<const Table>(std::move(table))));
   return MG_OK;
 }
 
-int mg_tune_table_size(void) { return (int)rules_snapshot()->size(); }
+int mg_tune_table_size(void) { return (int)table_snapshot()->rules.size(); }
+
+int mg_config_occupancy(mg_dtype in_type, int config) {
+  int n = 0;
+  const KernelEntry *e = entries((int)in_type, &n);
+  if (!e || config < 0 || config >= n) return -1;
+  return runtime_occupancy((int)in_type, config, e[config]);
+}
 
 const char *mg_status_str(mg_status s) {
   switch (s) {

@@ -206,9 +206,19 @@ int mg_chosen_config_ws(mg_dtype in_type, mg_dtype c_type, mg_op ta, mg_op tb, i
  * '#' are comments.  A rule tagged "ws" applies only to gemm_ex calls with a
  * workspace (it was tuned with split-K and operand repacking available), and
  * its "s=" count (1..64) replaces the planner's fill rule when gemm_ex is
- * called with splits = 0; untagged rules apply to every call.  A problem takes the nearest rule of the same type and layout
- * class by log-distance of M, N, K, if one is near enough; rules naming an
- * element-load variant are skipped for operands 16-byte loads can read.
+ * called with splits = 0; untagged rules apply to every call.  Lines
+ * "rate <in> <config> <fraction> <workgroups per CU>" record, per
+ * configuration, the best fraction of the type's peak it reached where the
+ * table was tuned and its occupancy there.
+ *
+ * Planning (plain calls): a problem takes the nearest rule of the same type
+ * and layout class by log-distance of M, N, K, if one is near enough (sum of
+ * |log2| ratios <= 1.5).  A rule for another shape is dropped when a cost
+ * model expects it to be more than 10 % slower than the model's own pick.
+ * The model charges each configuration ceil(tiles / (256 x occupancy))
+ * rounds of (occupancy) tile times at its rate; it also decides for shapes no
+ * rule is near.  Rules naming an element-load variant are skipped for
+ * operands 16-byte loads can read.
  * Replaces any table loaded before.  Returns MG_EINVAL if the file cannot be
  * read or a line names an unknown config or tag (the previous table is then
  * kept).  The new table is published atomically: calls already planning keep
@@ -216,6 +226,13 @@ int mg_chosen_config_ws(mg_dtype in_type, mg_dtype c_type, mg_op ta, mg_op tb, i
 mg_status mg_load_tune_table(const char *path);
 /* Number of rules in the loaded table (0 if none). */
 int mg_tune_table_size(void);
+
+/* Workgroups of a configuration that fit on one CU of the current device at
+ * once, as the HIP runtime computes it from the kernel's registers, LDS and
+ * workgroup size (one representative layout); -1 for an unknown config or
+ * when the runtime cannot say (no device).  Used by the autotuner to record
+ * the figure in the tuning table. */
+int mg_config_occupancy(mg_dtype in_type, int config);
 
 /* Human-readable status text (static string). */
 const char *mg_status_str(mg_status s);

@@ -275,7 +275,7 @@ def test_shipped_table_covers_every_class_and_each_rule_wins_its_own_shape(mg):
         if line.startswith("#") or not line.strip():
             continue
         f = line.split()
-        if len(f) > 8:  # workspace rules apply only to gemm_ex calls
+        if f[0] == "rate" or len(f) > 8:  # rates; workspace rules apply only to gemm_ex calls
             continue
         ind, cd, ta, tb = f[0], f[1], f[2] == "T", f[3] == "T"
         M, N, K = map(int, f[4:7])
@@ -324,3 +324,31 @@ def test_tune_table_reload_while_planning(mg, tmp_path):
     mg.load_tune_table(mg.TUNE_TABLE)
     assert not bad
     assert seen <= want and seen
+
+
+def test_tune_table_rate_lines(mg, tmp_path):
+    name = mg.config_name("f16", 0)
+    good = tmp_path / "r.txt"
+    good.write_text(f"rate f16 {name} 0.52 1\nf16 f16 N T 4096 4096 4096 {name}\n")
+    mg.load_tune_table(str(good))
+    assert mg.load().mg_tune_table_size() == 1  # rates are not rules
+    for bad in (f"rate f16 {name} 0 1\n", f"rate f16 {name} 1.5 1\n", "rate f16 no_such_config 0.5 1\n",
+                f"rate f64 {name} 0.5 1\n", f"rate f16 {name} 0.5\n", f"rate f16 {name} 0.5 0\n"):
+        t = tmp_path / "bad.txt"
+        t.write_text(bad)
+        with pytest.raises(mg.MgemmError):
+            mg.load_tune_table(str(t))
+    mg.load_tune_table(mg.TUNE_TABLE)
+
+
+def test_cost_model_off_table_picks(mg):
+    """Shapes no rule is near, with the shipped rates: the model fills the GPU
+    instead of taking a neighbour's tile that would leave CUs idle, and takes
+    the bigger tile when both fill it."""
+    mg.load_tune_table(mg.TUNE_TABLE)
+    area = lambda t, c: int(re.search(r"_(\d+)x(\d+)x", mg.config_name(t, c)).group(1)) * \
+        int(re.search(r"_(\d+)x(\d+)x", mg.config_name(t, c)).group(2))
+    # fp32 3072^3: 144 tiles of 256^2 would leave 112 CUs idle
+    assert area("f32", mg.chosen_config("f32", "f32", 0, 0, 3072, 3072, 3072)) < 256 * 256
+    # fp16 3000 x 5000 x 2000: 240 tiles of 256^2 beat 480 of 256 x 128
+    assert area("f16", mg.chosen_config("f16", "f16", 0, 1, 3000, 5000, 2000)) == 256 * 256
