@@ -1,5 +1,5 @@
 // The C ABI of libmgemm (declared in include/mgemm.h): argument validation,
-// the shape-keyed planner (tuning table + built-in heuristic) and the launch
+// the shape-keyed planner (tuning table + cost model) and the launch
 // on the caller's stream.  No allocation, no printing, no exceptions across
 // the boundary.
 #include <hip/hip_runtime.h>

@@ -36,3 +36,25 @@ def test_flops_and_bytes_match_the_worklog_lower_bounds():
 def test_beta_zero_reads_no_c():
     w = dict(M=64, N=32, K=16, in_dtype="f16", c_dtype="f16", beta=0.0)
     assert bench.min_bytes(w) == (64 * 16 + 16 * 32) * 2 + 64 * 32 * 2
+
+
+def test_kernel_hash_follows_device_sources_only(tmp_path):
+    """The hash that ties counter measurements to kernels changes with a
+    device header and the build flags, not with host-only planner code."""
+    import shutil
+    from dense_gemm_12_amd import srchash
+    pkg = tmp_path / "pkg"
+    shutil.copytree(os.path.join(srchash.HERE, "csrc"), pkg / "csrc")
+    shutil.copy(os.path.join(srchash.HERE, "build.py"), pkg / "build.py")
+    h0 = srchash.kernel_src_hash(str(pkg))
+    assert h0 == srchash.kernel_src_hash()
+    with open(pkg / "csrc" / "mgemm_api.cpp", "a") as f:
+        f.write("\n// host-only edit\n")
+    assert srchash.kernel_src_hash(str(pkg)) == h0
+    with open(pkg / "csrc" / "epilogue.hpp", "a") as f:
+        f.write("\n// device edit\n")
+    h1 = srchash.kernel_src_hash(str(pkg))
+    assert h1 != h0
+    with open(pkg / "build.py", "a") as f:
+        f.write("\n# flags\n")
+    assert srchash.kernel_src_hash(str(pkg)) != h1
