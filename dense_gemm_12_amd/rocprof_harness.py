@@ -236,10 +236,10 @@ def collect(dirs, profiles):
         with open(os.path.join(d, "summary.md")) as f:
             body = f.read().split("\n", 1)[1]
         cmd = (f"python3 -m dense_gemm_12_amd.rocprof_harness run --workload {w} --iters "
-               f"{s.get('iters', 5)} --out gpurun_out/harness_{w}")
+               f"{s.get('iters', 5)} --out $OUT/harness_{w}")
         text = (f"# Hardware counters: {w}\n\n"
-                "Command (each counter group is one rocprofv3 --pmc pass over the workload, plus two "
-                "passes over a 1 GiB copy for calibrating FETCH_SIZE/WRITE_SIZE):\n\n"
+                "Command ($OUT: any scratch directory; each counter group is one rocprofv3 --pmc pass over "
+                "the workload, plus two passes over a 1 GiB copy for calibrating FETCH_SIZE/WRITE_SIZE):\n\n"
                 f"```\n{cmd}\n```\n\nKernel configuration `{s['config']}`, kernel source hash "
                 f"`{s['src_hash']}`.\n{body}\n"
                 f"Calibration: a {cal['bytes_each_way']} B device copy reads FETCH_SIZE = "
