@@ -157,3 +157,45 @@ def test_repacked_operands_integer_bit_exact(in_dtype):
             ref = oracle_full(A, B, C, alpha=1.5, beta=0.5, ta=ta, tb=tb, in_dtype=in_dtype, c_dtype=c_dtype)
             assert_bit_exact(got, ref, c_dtype, what)
     assert mg.load() is not None
+
+
+def _bench_workspace_workloads():
+    """Named workloads the benchmark runs through gemm_ex with a workspace
+    (the planner would split or repack them), small enough for the full
+    oracle."""
+    import dense_gemm_12_amd as mg
+    out = []
+    for name, w in gi.WORKLOADS.items():
+        if w["M"] * w["N"] * w["K"] > 3e9:
+            continue
+        codes = mg.DTYPE_CODES
+        lda = w["M"] if w["ta"] else w["K"]
+        ldb = w["K"] if w["tb"] else w["N"]
+        if mg.workspace_size(codes[w["in_dtype"]], codes[w["c_dtype"]], int(w["ta"]), int(w["tb"]),
+                             w["M"], w["N"], w["K"], lda, ldb) > 0:
+            out.append(name)
+    return out
+
+
+@pytest.mark.parametrize("integer_twin", [False, True], ids=["random", "int"])
+@pytest.mark.parametrize("name", _bench_workspace_workloads())
+def test_bench_workspace_launches(name, integer_twin):
+    """Each such workload in the benchmark's launch configuration (gemm_ex,
+    the planner's split count and configuration) against the full oracle."""
+    import dense_gemm_12_amd as mg
+    w = gi.WORKLOADS[name]
+    A, B, C = gi.workload_inputs(name, integer_twin=integer_twin)
+    M, N, K = w["M"], w["N"], w["K"]
+    codes = mg.DTYPE_CODES
+    ws = mg.workspace_size(codes[w["in_dtype"]], codes[w["c_dtype"]], int(w["ta"]), int(w["tb"]), M, N, K,
+                           A.stride(0), B.stride(0))
+    log(f"case {name} int={integer_twin} workspace {ws} bytes")
+    got = run_gpu(A, B, C, alpha=w["alpha"], beta=w["beta"], ta=w["ta"], tb=w["tb"], c_dtype=w["c_dtype"],
+                  workspace_bytes=ws, splits=0)
+    kw = dict(alpha=w["alpha"], beta=w["beta"], ta=w["ta"], tb=w["tb"], in_dtype=w["in_dtype"],
+              c_dtype=w["c_dtype"])
+    ref = oracle_full(A, B, C, **kw)
+    if integer_twin:
+        assert_bit_exact(got, ref, w["c_dtype"], name)
+    else:
+        assert_within(out_as_f64(got, w["c_dtype"]), ref, A=A, B=B, Cin=C, what=name, **kw)
