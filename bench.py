@@ -84,7 +84,19 @@ def load_traffic(config_name, workload):
     from dense_gemm_12_amd.srchash import kernel_src_hash
     if not rec or rec.get("config") != config_name or rec.get("src_hash") != kernel_src_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("l2_miss_bytes_per_launch")
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def cpu_baseline(parts, target_s):
@@ -125,7 +137,7 @@ def cpu_baseline(parts, target_s):
         desc.append(f"{name}: rows 0..{rows} of {w['M']} ({f / 1e9:.1f} GFLOP, {dt:.1f} s)")
     return {"value": total_flops / total_s / 1e12, "unit": "TFLOPS", "cores": threads,
             "kind": "oracle", "sample": "; ".join(desc) + "; fp64 triple loop, threads over rows",
-            "seconds": round(total_s, 2), "cpu": platform.processor() or platform.machine()}
+            "seconds": round(total_s, 2), "cpu": cpu_model()}
 
 
 def cpu_blocked(parts):

@@ -225,6 +225,13 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, trans_a: bool = False,
     import torch
     if A.dtype != B.dtype:
         raise TypeError("A and B must have the same dtype")
+    # every buffer the kernels touch must live on C's GPU: a host pointer
+    # handed to a kernel faults the device
+    for name, t in (("A", A), ("B", B), ("workspace", workspace)):
+        if t is not None and (not t.is_cuda or t.device != C.device):
+            raise ValueError(f"{name} must be a CUDA tensor on {C.device}, got {t.device}")
+    if not C.is_cuda:
+        raise ValueError(f"C must be a CUDA tensor, got {C.device}")
     M = A.shape[1] if trans_a else A.shape[0]
     K = A.shape[0] if trans_a else A.shape[1]
     N = B.shape[0] if trans_b else B.shape[1]

@@ -78,19 +78,20 @@ template <> struct Mfma<float> {
 // logical tiles; grouped raster then walks group_m tile-rows at a time so
 // tiles that share A rows / B columns run close together in time on the same
 // L2.  Both maps are bijections on [0, tiles), so any dispatch order is
-// still correct.
-__device__ __forceinline__ int remap_xcd(int b, int tiles) {
+// still correct.  They compile for the host too, where a CPU test checks
+// the bijections over many grid shapes.
+__host__ __device__ __forceinline__ int remap_xcd(int b, int tiles) {
   const int q = tiles >> 3, r = tiles & 7;
   const int xcd = b & 7, idx = b >> 3;
   return xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
 }
 
-__device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int group_m, int &tm,
-                                            int &tn) {
+__host__ __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int group_m, int &tm,
+                                                     int &tn) {
   const int per_group = group_m * tiles_n;
   const int g = b / per_group;
   const int first_m = g * group_m;
-  const int gsz = min(tiles_m - first_m, group_m);
+  const int gsz = tiles_m - first_m < group_m ? tiles_m - first_m : group_m;
   const int in_g = b - g * per_group;
   tm = first_m + in_g % gsz;
   tn = in_g / gsz;
@@ -100,14 +101,15 @@ __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int
 // tiles * splits workgroups; the split index is the slow one, so each XCD's
 // contiguous share of logical indices holds whole splits, whose workgroups
 // read the same K range of A and B.
-__device__ __forceinline__ void work_coords(int b, int tiles_m, int tiles_n, int group_m, int splits,
-                                            int K, int k_chunk, int &tm, int &tn, int &k0, int &kl) {
+__host__ __device__ __forceinline__ void work_coords(int b, int tiles_m, int tiles_n, int group_m,
+                                                     int splits, int K, int k_chunk, int &tm, int &tn,
+                                                     int &k0, int &kl) {
   const int tiles = tiles_m * tiles_n;
   const int l = remap_xcd(b, tiles * splits);
   const int s = l / tiles;
   tile_coords(l - s * tiles, tiles_m, tiles_n, group_m, tm, tn);
   k0 = s * k_chunk;
-  kl = splits > 1 ? min(K - k0, k_chunk) : K;
+  kl = splits > 1 ? (K - k0 < k_chunk ? K - k0 : k_chunk) : K;
 }
 
 // ------------------------------------------------------------ conversions --

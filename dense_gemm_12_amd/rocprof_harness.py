@@ -6,9 +6,12 @@ Two modes:
     Runs one rocprofv3 pass per counter group (each group stays within the
     per-block limits of one pass), each over ``target`` below, then parses
     the CSV output and writes ``DIR/summary.json`` and ``DIR/summary.md``:
-    MFMA utilisation, VALU busy, LDS bank-conflict rate, effective shader
-    clock, HBM-side traffic (FETCH_SIZE / WRITE_SIZE calibrated against a
-    plain copy of known size) and achieved TFLOPS / GB/s against the peaks.
+    MFMA utilisation, VALU busy (both from raw counters and, as a cross-check,
+    from rocprofiler-sdk's own derived ``MfmaUtil`` / ``VALUBusy``), LDS
+    bank-conflict rate, effective shader clock, L2-miss traffic (FETCH_SIZE /
+    WRITE_SIZE calibrated against a plain copy of known size), the part of it
+    addressed to DRAM (TCC_EA0_*_DRAM_32B; Infinity-Cache hits still count
+    there) and achieved TFLOPS / GB/s against the peaks.
 
 ``python -m dense_gemm_12_amd.rocprof_harness target --workload NAME [--iters N] [--config C]``
     The program each pass profiles: uploads the workload's seeded inputs and
@@ -46,9 +49,14 @@ COPY_BYTES = 1 << 30
 PASSES = {
     "fetch": ["FETCH_SIZE", "GRBM_GUI_ACTIVE"],
     "write": ["WRITE_SIZE", "GRBM_GUI_ACTIVE"],
+    "dram": ["TCC_EA0_RDREQ_DRAM_32B_sum", "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum", "GRBM_GUI_ACTIVE"],
     "sq": ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_LDS_BANK_CONFLICT",
            "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_BUSY_CU_CYCLES",
            "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE"],
+    # rocprofiler-sdk's derived metrics (counter_defs.yaml, gfx950):
+    #   MfmaUtil = 100 * sum(SQ_VALU_MFMA_BUSY_CYCLES) / (max(GRBM_GUI_ACTIVE) * SIMD_NUM)
+    #   VALUBusy = 100 * sum(SQ_ACTIVE_INST_VALU) / CU_NUM / max(GRBM_GUI_ACTIVE)
+    "derived": ["MfmaUtil", "VALUBusy"],
 }
 
 
@@ -139,7 +147,7 @@ def run(args):
     for name, counters in PASSES.items():
         results[name] = _run_pass(name, counters, tgt, out)
     calib = {}
-    for name in ("fetch", "write"):
+    for name in ("fetch", "write", "dram"):
         calib[name] = _run_pass("copy_" + name, PASSES[name], ["--workload", "copy", "--iters", "3"],
                                 out)
     kname = _pick(results["sq"], "gemm")
@@ -148,6 +156,9 @@ def run(args):
     write_copy = _avg(calib["write"][copy_k], "WRITE_SIZE")
     f_factor = COPY_BYTES / (fetch_copy * 1024) if fetch_copy else None
     w_factor = COPY_BYTES / (write_copy * 1024) if write_copy else None
+    dcopy_k = max(calib["dram"], key=lambda k: len(calib["dram"][k]["dispatch"]))
+    dram_rd_copy = _avg(calib["dram"][dcopy_k], "TCC_EA0_RDREQ_DRAM_32B_sum")
+    dram_wr_copy = _avg(calib["dram"][dcopy_k], "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum")
 
     w = gi.WORKLOADS[args.workload]
     flops = 2.0 * w["M"] * w["N"] * w["K"]
@@ -164,6 +175,12 @@ def run(args):
     gui_cycles = gui / 8 if gui else None
     fetch_kib = _avg(results["fetch"][_pick(results["fetch"], "gemm")], "FETCH_SIZE")
     write_kib = _avg(results["write"][_pick(results["write"], "gemm")], "WRITE_SIZE")
+    dr = results["dram"][_pick(results["dram"], "gemm")]
+    dram_rd = _avg(dr, "TCC_EA0_RDREQ_DRAM_32B_sum")
+    dram_wr = _avg(dr, "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum")
+    der = results["derived"][_pick(results["derived"], "gemm")]
+    sdk_mfma = _avg(der, "MfmaUtil")
+    sdk_valu = _avg(der, "VALUBusy")
     es = 4 if w["in_dtype"] == "f32" else 2
     ec = 4 if w["c_dtype"] == "f32" else 2
     min_bytes = (w["M"] * w["K"] + w["K"] * w["N"]) * es + w["M"] * w["N"] * ec * (2 if w["beta"] else 1)
@@ -183,25 +200,38 @@ def run(args):
         "gui_active_cycles": gui_cycles,
         "effective_clock_ghz": (gui_cycles / dur_ns) if (gui_cycles and dur_ns) else None,
         "mfma_util_pct": 100.0 * mfma / (gui_cycles * SIMDS) if (mfma and gui_cycles) else None,
-        "valu_busy_pct": 100.0 * valu * 4 / CUS / gui_cycles if (valu and gui_cycles) else None,
+        "valu_busy_pct": 100.0 * valu / CUS / gui_cycles if (valu and gui_cycles) else None,
         "lds_bank_conflict_per_access": bank / (ldsact - bank) if (ldsact and ldsact > bank) else None,
         "lds_bank_conflict_cycles_pct": 100.0 * bank / (gui_cycles * CUS) if (bank is not None and gui_cycles) else None,
         "sq_insts_mfma": _avg(sq, "SQ_INSTS_MFMA"), "sq_insts_lds": _avg(sq, "SQ_INSTS_LDS"),
+        "sdk_MfmaUtil_pct": sdk_mfma, "sdk_VALUBusy_pct": sdk_valu,
         "fetch_kib_raw": fetch_kib, "write_kib_raw": write_kib,
         "copy_calibration": {"bytes_each_way": COPY_BYTES, "fetch_kib": fetch_copy,
                              "write_kib": write_copy, "fetch_factor": f_factor,
                              "write_factor": w_factor},
-        "hbm_fetch_bytes": fetch_b, "hbm_write_bytes": write_b,
-        "hbm_bytes_per_launch": (fetch_b + write_b) if (fetch_b is not None and write_b is not None) else None,
+        "l2_miss_fetch_bytes": fetch_b, "l2_miss_write_bytes": write_b,
+        "l2_miss_bytes_per_launch": (fetch_b + write_b) if (fetch_b is not None and write_b is not None) else None,
+        "dram_32b_reads": dram_rd, "dram_32b_writes": dram_wr,
+        "dram_copy_calibration": {"bytes_each_way": COPY_BYTES, "rd_32b": dram_rd_copy, "wr_32b": dram_wr_copy},
+        "dram_read_bytes": dram_rd * 32 if dram_rd is not None else None,
+        "dram_write_bytes": dram_wr * 32 if dram_wr is not None else None,
         "min_bytes_per_launch": min_bytes,
         "flops_per_launch": flops,
     }
     if dur_ns:
         summary["tflops_under_pmc"] = flops / dur_ns / 1e3
         summary["frac_of_peak_under_pmc"] = summary["tflops_under_pmc"] / PEAK_TFLOPS[w["in_dtype"]]
-        if summary["hbm_bytes_per_launch"]:
-            summary["hbm_gbps"] = summary["hbm_bytes_per_launch"] / dur_ns
-            summary["hbm_frac_of_peak"] = summary["hbm_gbps"] / HBM_GBPS
+        if summary["l2_miss_bytes_per_launch"]:
+            summary["l2_miss_gbps"] = summary["l2_miss_bytes_per_launch"] / dur_ns
+        if dram_rd is not None and dram_wr is not None:
+            summary["dram_gbps"] = (dram_rd + dram_wr) * 32 / dur_ns
+            summary["dram_frac_of_hbm_peak"] = summary["dram_gbps"] / HBM_GBPS
+    # The raw-counter derivations must agree with rocprofiler-sdk's own
+    # (different passes, so a few per cent of run-to-run spread is allowed).
+    for mine, sdk in (("mfma_util_pct", "sdk_MfmaUtil_pct"), ("valu_busy_pct", "sdk_VALUBusy_pct")):
+        a, b = summary.get(mine), summary.get(sdk)
+        summary[mine + "_agrees_with_sdk"] = (a is not None and b is not None and
+                                              abs(a - b) <= 0.1 * max(abs(b), 1.0))
     with open(os.path.join(out, "summary.json"), "w") as f:
         json.dump(summary, f, indent=2)
     lines = [f"# Counters: {args.workload}", "", f"kernel: `{kname}`", "",
@@ -229,8 +259,10 @@ def collect(dirs, profiles):
         w = s["workload"]
         cal = s["copy_calibration"]
         table[w] = {"config": s["config"], "src_hash": s["src_hash"],
-                    "hbm_bytes_per_launch": s["hbm_bytes_per_launch"],
-                    "hbm_fetch_bytes": s["hbm_fetch_bytes"], "hbm_write_bytes": s["hbm_write_bytes"],
+                    "l2_miss_bytes_per_launch": s["l2_miss_bytes_per_launch"],
+                    "l2_miss_fetch_bytes": s["l2_miss_fetch_bytes"],
+                    "l2_miss_write_bytes": s["l2_miss_write_bytes"],
+                    "dram_read_bytes": s.get("dram_read_bytes"), "dram_write_bytes": s.get("dram_write_bytes"),
                     "fetch_factor": cal["fetch_factor"], "write_factor": cal["write_factor"],
                     "source": f"profiles/counters_{w}.md"}
         with open(os.path.join(d, "summary.md")) as f:
@@ -239,20 +271,25 @@ def collect(dirs, profiles):
                f"{s.get('iters', 5)} --out $OUT/harness_{w}")
         text = (f"# Hardware counters: {w}\n\n"
                 "Command ($OUT: any scratch directory; each counter group is one rocprofv3 --pmc pass over "
-                "the workload, plus two passes over a 1 GiB copy for calibrating FETCH_SIZE/WRITE_SIZE):\n\n"
+                "the workload, plus three passes over a 1 GiB copy for calibrating FETCH_SIZE, WRITE_SIZE "
+                "and the DRAM request counters):\n\n"
                 f"```\n{cmd}\n```\n\nKernel configuration `{s['config']}`, kernel source hash "
                 f"`{s['src_hash']}`.\n{body}\n"
                 f"Calibration: a {cal['bytes_each_way']} B device copy reads FETCH_SIZE = "
                 f"{cal['fetch_kib']:.0f} KiB and WRITE_SIZE = {cal['write_kib']:.0f} KiB, so fetched "
                 f"bytes = FETCH_SIZE x 1024 x {cal['fetch_factor']:.4f} and written bytes = WRITE_SIZE "
                 f"x 1024 x {cal['write_factor']:.4f}.\n"
-                "FETCH_SIZE counts L2 misses (requests that leave the XCD's L2 for the Infinity Cache "
-                "/ HBM); with the 256 MB Infinity Cache some of these are not DRAM reads.\n"
+                "FETCH_SIZE / WRITE_SIZE count L2 misses (requests that leave the XCD's L2 for the "
+                "Infinity Cache / HBM), hence the l2_miss_* names; TCC_EA0_{RDREQ,WRREQ_WRITE}_DRAM_32B "
+                "count the 32-byte requests of those addressed to DRAM, which still include Infinity-Cache "
+                "hits (the copy calibration shows how they relate to bytes moved).\n"
+                "valu_busy_pct / mfma_util_pct are derived from the raw counters with rocprofiler-sdk's "
+                "formulas; sdk_* are the SDK's own derived counters from a separate pass.\n"
                 "GRBM_GUI_ACTIVE covers a little time around each dispatch, so for short kernels "
                 "(about 100 us) the effective clock reads high and the MFMA utilisation low.\n")
         with open(os.path.join(profiles, f"counters_{w}.md"), "w") as f:
             f.write(text)
-        print(f"{w}: {s['config']} {s['hbm_bytes_per_launch']:.4g} B/launch")
+        print(f"{w}: {s['config']} {s['l2_miss_bytes_per_launch']:.4g} L2-miss B/launch")
     with open(path, "w") as f:
         json.dump(table, f, indent=2)
         f.write("\n")

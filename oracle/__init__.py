@@ -200,16 +200,3 @@ def col_norms(B, dtype, trans=False):
     if trans:
         b = b.T
     return np.sqrt(np.sum(b * b, axis=0))
-
-
-def error_bound(tol, alpha, beta, a_norms, b_norms, c_in=None):
-    """Per-element bound tol*(|alpha|*|a_i|*|b_j| + |beta|*|C_in_ij|).
-
-    The error model scales with the Cauchy-Schwarz bound of each dot product:
-    tol is 1e-5 for fp32 and 4e-3 for fp16/bf16 inputs; the beta term covers
-    the rounding of the scaled C_in.
-    """
-    bound = abs(alpha) * np.outer(a_norms, b_norms)
-    if beta != 0.0 and c_in is not None:
-        bound = bound + abs(beta) * np.abs(c_in)
-    return tol * bound

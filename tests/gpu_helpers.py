@@ -132,12 +132,18 @@ def assert_within(got64, ref64, *, A, B, Cin, alpha, beta, ta, tb, in_dtype, c_d
     return worst
 
 
-def sample_plan(M, N, seed, n_lines=64, block=256):
-    """Deterministic sample: rows and columns at random, the four corner
-    blocks and the last partial tile rows/cols are all included."""
+def sample_plan(M, N, seed, n_lines=64, block=256, band=128):
+    """Deterministic sample: rows and columns at random, at least one random
+    row in every ``band``-row band and one random column in every
+    ``band``-column band (so every tile of 128 or more rows and columns has
+    sampled elements, and a tile left unwritten cannot escape the
+    element-wise check), the four corner blocks and the last partial tile
+    rows/cols."""
     rng = np.random.default_rng(seed)
     rows = set(rng.choice(M, size=min(n_lines, M), replace=False).tolist())
     cols = set(rng.choice(N, size=min(n_lines, N), replace=False).tolist())
+    rows |= {int(rng.integers(b, min(M, b + band))) for b in range(0, M, band)}
+    cols |= {int(rng.integers(b, min(N, b + band))) for b in range(0, N, band)}
     rows |= set(range(max(0, M - 3), M)) | {0}
     cols |= set(range(max(0, N - 3), N)) | {0}
     blocks = []
@@ -169,59 +175,119 @@ def oracle_cols(A, B, Cin, cols, *, alpha, beta, ta, tb, in_dtype, c_dtype):
                        c_dtype=c_dtype)
 
 
+# Unit roundoff of each output type (half an ulp at 1).
+UNIT_ROUNDOFF = {"f32": 2.0 ** -24, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+# Hoeffding multiplier: a sum sum_j e_j x_j with fixed |e_j| <= b_j and
+# independent random signs x_j exceeds T * sqrt(sum_j b_j^2) with probability
+# at most 2 exp(-T^2 / 2) < 3e-14 for T = 8.
+HOEFFDING_T = 8.0
+
+
 def freivalds_stream(C: torch.Tensor, A, B, Cin, *, alpha, beta, ta, tb, in_dtype, c_dtype,
-                     seed=0, exact=False, chunk=2048):
-    """Freivalds check in fp64 with a +-1 vector, streaming over row chunks
-    so that large operands never exist in fp64 all at once.
+                     seed=0, exact=False, chunk=2048, rounds=2, extra_rel=0.0, acc_terms=None):
+    """Whole-matrix Freivalds check in fp64, streaming over row chunks so
+    that large operands never exist in fp64 all at once.
+
+    For random +-1 vectors x (drawn here, after C was computed, so they are
+    independent of its error E = C - C_ref), (C x)_i is compared with the
+    exact (alpha op(A) (op(B) x) + beta C_in x)_i.  If every |E_ij| <= b_ij,
+    Hoeffding's inequality bounds |(E x)_i| by HOEFFDING_T * sqrt(sum_j b_ij^2)
+    except with probability < 3e-14 per row and vector; a larger difference
+    fails.  Two per-element bounds b_ij are checked:
+
+    * the stated tolerance tol * (|alpha| |a_i| |b_j| + |beta| |C_in,ij|);
+    * the worst-case rounding error of fp32 accumulation (any summation order
+      of n terms is within gamma_n = n u / (1 - n u) of sum |terms|, u = 2^-24;
+      Higham, Accuracy and Stability of Numerical Algorithms, section 3.1),
+      bounded with Cauchy-Schwarz by gamma * (|alpha| |a_i| |b_j| +
+      |beta| |C_in,ij|), plus the output rounding u_C |C_ij|.  ``acc_terms``
+      is n (default K + 66: the K products, up to 64 split-K partials, alpha
+      and beta, each rounded at most once); ``extra_rel`` adds an
+      error relative to |a_i| |b_j| for paths that approximate the products
+      (fp32 through split fp16).  This is what catches a plausible but wrong
+      result (a zeroed tile, C left as C_in) when the stated tolerance is
+      loose next to |C| (16-bit inputs at large K).
 
     ``exact``: integer data, where every fp64 quantity is an exact integer,
     so equality is required."""
     rng = np.random.default_rng(seed)
     M, N = C.shape
     K = A.shape[0] if ta else A.shape[1]
-    x = rng.choice([-1.0, 1.0], size=N)
-    # y = op(B) x  (K-vector), and column norms of op(B) (for the slack)
-    y = np.zeros(K)
+    X = rng.choice([-1.0, 1.0], size=(N, rounds))
+    # Y = op(B) X (K x rounds), and the column norms of op(B)
+    Y = np.zeros((K, rounds))
     bn2 = np.zeros(N)
     Bb = bits(B)
     for s in range(0, Bb.shape[0], chunk):
         blk = oracle.widen(Bb[s:s + chunk], in_dtype)
         if tb:   # stored N x K: rows are columns of op(B)
-            y += blk.T @ x[s:s + chunk]
+            Y += blk.T @ X[s:s + chunk]
             bn2[s:s + chunk] += np.sum(blk * blk, axis=1)
         else:    # stored K x N
-            y[s:s + chunk] = blk @ x
+            Y[s:s + chunk] = blk @ X
             bn2 += np.sum(blk * blk, axis=0)
-    bsum = np.sqrt(bn2).sum()
+    bn = np.sqrt(bn2)
+    sum_bn, sum_bn2 = bn.sum(), bn2.sum()
     Ab = bits(A)
-    lhs = np.zeros(M)
-    rhs = np.zeros(M)
+    lhs = np.zeros((M, rounds))
+    rhs = np.zeros((M, rounds))
     an2 = np.zeros(M)
+    c_abs = np.zeros(M)       # sum_j |C_ij|
+    c_sq = np.zeros(M)        # sum_j C_ij^2
     Cb = bits(C.contiguous())
     for s in range(0, M, chunk):
         e = min(M, s + chunk)
         c = oracle.widen(Cb[s:e], c_dtype)
-        lhs[s:e] = c @ x
+        if not np.all(np.isfinite(c)):
+            bad = np.argwhere(~np.isfinite(c))[0]
+            raise AssertionError(f"Freivalds: non-finite C at ({s + bad[0]}, {bad[1]})")
+        lhs[s:e] = c @ X
+        c_abs[s:e] = np.abs(c).sum(axis=1)
+        c_sq[s:e] = (c * c).sum(axis=1)
     if ta:
         for s in range(0, Ab.shape[0], chunk):   # stored K x M
             blk = oracle.widen(Ab[s:s + chunk], in_dtype)
-            rhs += blk.T @ y[s:s + chunk]
+            rhs += blk.T @ Y[s:s + chunk]
             an2 += np.sum(blk * blk, axis=0)
     else:
         for s in range(0, M, chunk):
             blk = oracle.widen(Ab[s:s + chunk], in_dtype)
-            rhs[s:s + chunk] = blk @ y
+            rhs[s:s + chunk] = blk @ Y
             an2[s:s + chunk] = np.sum(blk * blk, axis=1)
+    an = np.sqrt(an2)
     rhs *= alpha
-    slack = TOL[in_dtype] * abs(alpha) * np.sqrt(an2) * bsum
+    aa = abs(alpha)
+    # sum_j (|alpha| a_i n_j + |beta| |cin_ij|)^2 and sum_j of the same term
+    g_sq = aa * aa * an2 * sum_bn2
+    g_abs = aa * an * sum_bn
     if beta != 0.0:
         Cib = bits(Cin)
+        ab = abs(beta)
         for s in range(0, M, chunk):
-            ci = oracle.widen(Cib[s:s + chunk], c_dtype)
-            rhs[s:s + chunk] += beta * (ci @ x)
-            slack[s:s + chunk] += TOL[in_dtype] * abs(beta) * np.abs(ci).sum(axis=1)
+            e = min(M, s + chunk)
+            ci = oracle.widen(Cib[s:e], c_dtype)
+            rhs[s:e] += beta * (ci @ X)
+            cia = np.abs(ci)
+            g_sq[s:e] += 2.0 * aa * ab * an[s:e] * (cia @ bn) + ab * ab * (cia * cia).sum(axis=1)
+            g_abs[s:e] += ab * cia.sum(axis=1)
+    diff = np.abs(lhs - rhs)
     if exact:
-        bad = np.nonzero(lhs != rhs)[0]
-    else:
-        bad = np.nonzero(np.abs(lhs - rhs) > slack + 1e-9 * (np.abs(rhs) + 1.0))[0]
-    assert bad.size == 0, f"Freivalds failed on {bad.size} rows, first row {bad[0]}"
+        bad = np.nonzero(np.any(diff != 0, axis=1))[0]
+        assert bad.size == 0, f"Freivalds (exact) failed on {bad.size} rows, first row {bad[0]}"
+        return
+    # error of the fp64 evaluation of the check itself
+    u64 = 2.0 ** -53
+    eval_slack = (N + K + 8) * 2 * u64 * (g_abs + c_abs)
+    stated = HOEFFDING_T * TOL[in_dtype] * np.sqrt(g_sq) + eval_slack
+    bad = np.nonzero(np.any(diff > stated[:, None], axis=1))[0]
+    assert bad.size == 0, (f"Freivalds (stated tolerance) failed on {bad.size} rows, first row {bad[0]}: "
+                           f"|diff| {diff[bad[0]].max():.4g} > {stated[bad[0]]:.4g}")
+    n = (K + 66) if acc_terms is None else acc_terms
+    u = 2.0 ** -24
+    gamma = n * u / (1.0 - n * u) + extra_rel
+    uc = UNIT_ROUNDOFF[c_dtype] * (1.0 + 2.0 ** -10)
+    # (x + y)^2 <= 2 x^2 + 2 y^2 for the two parts of the element bound
+    derived = HOEFFDING_T * np.sqrt(2.0 * gamma * gamma * g_sq + 2.0 * uc * uc * c_sq) + eval_slack
+    bad = np.nonzero(np.any(diff > derived[:, None], axis=1))[0]
+    assert bad.size == 0, (f"Freivalds (fp32-accumulation bound) failed on {bad.size} rows, first row "
+                           f"{bad[0]}: |diff| {diff[bad[0]].max():.4g} > {derived[bad[0]]:.4g}")

@@ -352,3 +352,13 @@ def test_cost_model_off_table_picks(mg):
     assert area("f32", mg.chosen_config("f32", "f32", 0, 0, 3072, 3072, 3072)) < 256 * 256
     # fp16 3000 x 5000 x 2000: 240 tiles of 256^2 beat 480 of 256 x 128
     assert area("f16", mg.chosen_config("f16", "f16", 0, 1, 3000, 5000, 2000)) == 256 * 256
+
+
+def test_gemm_rejects_host_tensors_before_any_launch():
+    """A host pointer handed to a kernel faults the GPU, so the torch binding
+    refuses tensors that are not on C's GPU before calling the library."""
+    import torch
+    import dense_gemm_12_amd as mg
+    A = torch.zeros((4, 4))
+    with pytest.raises(ValueError):
+        mg.gemm(A, A.clone(), torch.zeros((4, 4)))

@@ -290,3 +290,76 @@ def test_random_fp32_within_textbook_error_of_float32_product():
     got = oracle.gemm(A, B)
     bound = 300 * 2.0 ** -52 * (np.abs(A).astype(np.float64) @ np.abs(B).astype(np.float64))
     assert np.all(np.abs(got - ref) <= bound)
+
+
+@pytest.mark.parametrize("ta,tb", list(itertools.product([False, True], repeat=2)))
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_padded_storage_every_layout_matches_exact_integer_product(ta, tb, dtype):
+    """Every layout with leading dimensions larger than the stored row length
+    (a transposed A stored K x M with lda > M, a transposed B stored N x K
+    with ldb > K, and the plain forms), padding filled with huge values: the
+    result equals the exact int64 product of the stored values, computed by
+    numpy from explicit transposes of contiguous copies.  Reading lda as M
+    (or ldb as K) for a transposed operand picks up the padding or the wrong
+    elements and fails."""
+    M, N, K = 11, 9, 14
+    sa = (K, M) if ta else (M, K)
+    sb = (N, K) if tb else (K, N)
+    A = gi.draw(*sa, "int2", 810, dtype, ld=sa[1] + 5)
+    B = gi.draw(*sb, "int2", 811, dtype, ld=sb[1] + 3)
+    C = gi.draw(M, N, "int2", 812, "f32", ld=N + 2)
+    An, Bn, Cn = gi.as_numpy_bits(A), gi.as_numpy_bits(B), gi.as_numpy_bits(C)
+    assert An.strides[0] // An.itemsize == sa[1] + 5 and Bn.strides[0] // Bn.itemsize == sb[1] + 3
+    got = oracle.gemm(An, Bn, a_dtype=dtype, trans_a=ta, trans_b=tb, alpha=2.0, beta=-1.0, C=Cn)
+    Ai = oracle.widen(np.ascontiguousarray(An), dtype).astype(np.int64)
+    Bi = oracle.widen(np.ascontiguousarray(Bn), dtype).astype(np.int64)
+    opA = np.ascontiguousarray(Ai.T) if ta else Ai
+    opB = np.ascontiguousarray(Bi.T) if tb else Bi
+    want = 2 * (opA @ opB) - np.ascontiguousarray(Cn).astype(np.int64)
+    assert np.array_equal(got, want.astype(np.float64))
+
+
+# ------------------------------------------------- tolerance norms (pins) --
+
+def test_row_and_col_norms_closed_forms_every_storage_order():
+    """row_norms / col_norms define every tolerance bound, so they are pinned
+    to closed forms: a row of op(A) made of K copies of v has 2-norm |v|*sqrt(K);
+    a column of op(B) made of K copies of w has |w|*sqrt(K); Pythagorean rows
+    (3, 4) and (1, 2, 2) have norms 5 and 3 exactly.  Each is checked for
+    both storage orders, so summing over the wrong axis, a missing square
+    root or a constant factor fails."""
+    K = 37
+    v = np.array([1.0, -2.0, 0.5, 3.0, 0.0, -0.25], np.float32)   # M = 6 rows of op(A)
+    w = np.array([2.0, -1.0, 0.125, 4.0], np.float32)              # N = 4 columns of op(B)
+    opA = np.repeat(v[:, None], K, axis=1)                          # M x K
+    opB = np.repeat(w[None, :], K, axis=0)                          # K x N
+    for dtype, conv in (("f32", lambda x: x), ("f16", lambda x: x.astype(np.float16)),
+                        ("bf16", lambda x: (x.view(np.uint32) >> 16).astype(np.uint16))):
+        a = conv(opA)
+        b = conv(opB)
+        want_a = np.abs(v.astype(np.float64)) * np.sqrt(K)
+        want_b = np.abs(w.astype(np.float64)) * np.sqrt(K)
+        assert np.allclose(oracle.row_norms(a, dtype), want_a, rtol=1e-15, atol=0)
+        assert np.allclose(oracle.row_norms(np.ascontiguousarray(a.T), dtype, trans=True), want_a,
+                           rtol=1e-15, atol=0)
+        assert np.allclose(oracle.col_norms(b, dtype), want_b, rtol=1e-15, atol=0)
+        assert np.allclose(oracle.col_norms(np.ascontiguousarray(b.T), dtype, trans=True), want_b,
+                           rtol=1e-15, atol=0)
+    pyth = np.array([[3, 4, 0], [1, 2, 2]], np.float32)
+    assert np.array_equal(oracle.row_norms(pyth, "f32"), [5.0, 3.0])
+    assert np.array_equal(oracle.row_norms(np.ascontiguousarray(pyth.T), "f32", trans=True), [5.0, 3.0])
+    assert np.array_equal(oracle.col_norms(np.ascontiguousarray(pyth.T), "f32"), [5.0, 3.0])
+    assert np.array_equal(oracle.col_norms(pyth, "f32", trans=True), [5.0, 3.0])
+
+
+def test_norms_of_padded_views_ignore_the_padding():
+    """A stored matrix inside a wider buffer (padding = 1e30) has the norms of
+    its contiguous copy, in both storage orders."""
+    A = gi.draw(7, 5, "uniform", 820, "f32", ld=9)
+    An = gi.as_numpy_bits(A)
+    want_rows = np.sqrt((np.ascontiguousarray(An).astype(np.float64) ** 2).sum(axis=1))
+    want_cols = np.sqrt((np.ascontiguousarray(An).astype(np.float64) ** 2).sum(axis=0))
+    assert np.allclose(oracle.row_norms(An, "f32"), want_rows, rtol=1e-15, atol=0)
+    assert np.allclose(oracle.col_norms(An, "f32"), want_cols, rtol=1e-15, atol=0)
+    assert np.allclose(oracle.row_norms(An, "f32", trans=True), want_cols, rtol=1e-15, atol=0)
+    assert np.allclose(oracle.col_norms(An, "f32", trans=True), want_rows, rtol=1e-15, atol=0)
