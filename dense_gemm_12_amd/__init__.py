@@ -18,7 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmgemm.so")
 TUNE_TABLE = os.path.join(HERE, "tune_gfx950.txt")
 
-MG_OK, MG_EINVAL, MG_EUNSUPPORTED, MG_EHIP = 0, 1, 2, 3
+MG_OK, MG_EINVAL, MG_EUNSUPPORTED, MG_EHIP, MG_ESCRATCH = 0, 1, 2, 3, 4
+NOALLOC_SCRATCH_BYTES = 32 << 20
 MG_N, MG_T = 0, 1
 MG_F32, MG_F16, MG_BF16 = 0, 1, 2
 DTYPE_CODES = {"f32": MG_F32, "f16": MG_F16, "bf16": MG_BF16}
@@ -26,7 +27,7 @@ DTYPE_CODES = {"f32": MG_F32, "f16": MG_F16, "bf16": MG_BF16}
 # Every exported symbol of include/mgemm.h.
 EXPORTS = (
     "gemm_f32", "gemm_f16", "gemm_bf16", "gemm_f32_cfg", "gemm_f16_cfg", "gemm_bf16_cfg",
-    "gemm_ex", "mg_workspace_size", "gemm_f32_split16", "mg_split16_workspace_size", "mg_chosen_config_ws",
+    "gemm_ex", "gemm_ex_noalloc", "mg_workspace_size", "gemm_f32_split16", "mg_split16_workspace_size", "mg_chosen_config_ws",
     "mg_num_configs", "mg_config_name", "mg_chosen_config", "mg_load_tune_table",
     "mg_tune_table_size", "mg_config_occupancy", "mg_status_str", "mg_last_hip_error", "mg_version",
 )
@@ -69,6 +70,9 @@ def load(path: str | None = None):
         lib.gemm_ex.argtypes = [ci, ci, ci, ci, i64, i64, i64, f, vp, i64, vp, i64, f, vp, i64, vp,
                                 ctypes.c_size_t, ci, ci, vp]
         lib.gemm_ex.restype = ci
+        lib.gemm_ex_noalloc.argtypes = [ci, ci, ci, ci, i64, i64, i64, f, vp, i64, vp, i64, f, vp, i64, ci,
+                                        ci, vp]
+        lib.gemm_ex_noalloc.restype = ci
         lib.mg_workspace_size.argtypes = [ci, ci, ci, ci, i64, i64, i64, i64, i64]
         lib.mg_workspace_size.restype = ctypes.c_size_t
         lib.gemm_f32_split16.argtypes = [ci, ci, i64, i64, i64, f, vp, i64, vp, i64, f, vp, i64, vp,
@@ -144,6 +148,12 @@ def gemm_ex(in_type, c_type, ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ld
             workspace_bytes, config=-1, splits=0, stream=None):
     _check(load().gemm_ex(in_type, c_type, ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                           workspace, workspace_bytes, config, splits, stream), "gemm_ex")
+
+
+def gemm_ex_noalloc(in_type, c_type, ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, config=-1,
+                    splits=0, stream=None):
+    _check(load().gemm_ex_noalloc(in_type, c_type, ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                                  config, splits, stream), "gemm_ex_noalloc")
 
 
 def workspace_size(in_type, c_type, ta, tb, M, N, K, lda, ldb) -> int:

@@ -752,6 +752,7 @@ const char *mg_status_str(mg_status s) {
     case MG_EINVAL: return "invalid argument";
     case MG_EUNSUPPORTED: return "unsupported problem (outside the kernels' addressing range)";
     case MG_EHIP: return "HIP launch error";
+    case MG_ESCRATCH: return "problem needs more scratch than the no-allocation entry point's fixed array holds";
     default: return "unknown status";
   }
 }

@@ -43,6 +43,8 @@
  *   MG_EUNSUPPORTED  valid but outside what the kernels address: a dimension
  *                    >= 2^31, or a leading dimension above 2^21 elements.
  *   MG_EHIP          the launch failed; mg_last_hip_error() gives the code.
+ *   MG_ESCRATCH      (gemm_ex_noalloc only) a forced split count needs more
+ *                    than the library's fixed scratch array.
  * Functions never throw and never print.  Calls are reentrant and thread
  * safe; a GEMM call plans with the tuning table loaded when it starts, even
  * while another thread loads a new one.
@@ -57,7 +59,7 @@
 extern "C" {
 #endif
 
-typedef enum { MG_OK = 0, MG_EINVAL = 1, MG_EUNSUPPORTED = 2, MG_EHIP = 3 } mg_status;
+typedef enum { MG_OK = 0, MG_EINVAL = 1, MG_EUNSUPPORTED = 2, MG_EHIP = 3, MG_ESCRATCH = 4 } mg_status;
 typedef enum { MG_N = 0, MG_T = 1 } mg_op;
 typedef enum { MG_F32 = 0, MG_F16 = 1, MG_BF16 = 2 } mg_dtype;
 
@@ -136,6 +138,27 @@ mg_status gemm_ex(mg_dtype in_type, mg_dtype c_type, mg_op ta, mg_op tb, int64_t
                   int64_t K, float alpha, const void *A, int64_t lda, const void *B, int64_t ldb,
                   float beta, void *C, int64_t ldc, void *workspace, size_t workspace_bytes,
                   int config, int splits, void *stream);
+
+/* gemm_ex without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Arguments, results and errors are gemm_ex's, with
+ * the workspace replaced by a fixed scratch array of MG_NOALLOC_SCRATCH_BYTES
+ * (32 MiB) that the library holds in device memory on every GPU it runs on,
+ * from the first call on that GPU until the process ends.  The call itself
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ * The GPU is the stream's (the current device for the null stream).
+ *
+ * The planner (splits = 0) splits and repacks only within the scratch, so any
+ * problem runs; a forced split count whose fp32 partials need more than the
+ * scratch (splits * M * N * 4 > MG_NOALLOC_SCRATCH_BYTES) returns MG_ESCRATCH
+ * before anything is launched.  Every call on one GPU uses that GPU's single
+ * array: calls that overlap in time on one GPU (different streams, or
+ * threads) race on it and give wrong results; serialize them.  The array
+ * keeps the last call's contents, which no call relies on. */
+#define MG_NOALLOC_SCRATCH_BYTES (32u << 20)
+mg_status gemm_ex_noalloc(mg_dtype in_type, mg_dtype c_type, mg_op ta, mg_op tb, int64_t M, int64_t N,
+                          int64_t K, float alpha, const void *A, int64_t lda, const void *B, int64_t ldb,
+                          float beta, void *C, int64_t ldc, int config, int splits, void *stream);
 
 /* Workspace bytes that gemm_ex with splits = 0 uses for this problem when
  * given enough (operand copies plus split partials; 0 when it would neither

@@ -47,7 +47,7 @@ def test_every_declared_symbol_is_exported(mg):
 def test_version_and_status_strings(mg):
     lib = mg.load()
     assert b"gfx950" in lib.mg_version()
-    for s in range(4):
+    for s in range(5):
         assert lib.mg_status_str(s)
     assert lib.mg_last_hip_error() == 0
 
