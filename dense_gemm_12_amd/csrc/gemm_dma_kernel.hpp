@@ -462,11 +462,153 @@ struct DmaTile {
     }
 
     wait_vmcnt<0>();  // the trailing (all out-of-range) DMA has landed before the LDS is released
+    // The last slice's schedule may leave fragment reads of a slice that does
+    // not exist in flight; their registers are dead, and the epilogue may
+    // reuse them for addresses, so those reads must land first.
+    wait_lgkm0_fenced();
     if (p.splits > 1)
       GemmEpilogue<float, MI, NJ, A_Q, B_Q>::store(partial_params(p, kb), acc, m0 + wm * WTM, n0 + wn * WTN,
                                                    lane);
     else
       GemmEpilogue<TO, MI, NJ, A_Q, B_Q>::store(p, acc, m0 + wm * WTM, n0 + wn * WTN, lane);
+  }
+};
+
+// Producer/consumer tile: the warp-specialised design of "Warp
+// Specialization HGEMM: 生产者-消费者模型的 GPU 形态" (section 问题的本质 and
+// the summary: copy warps only move tiles into a shared-memory ring, compute
+// warps only run the matrix instructions, and the two sides hand ring slots
+// to each other), built for gfx950:
+//   * four producer waves only issue the LDS DMA (buffer_load ... lds) of
+//     every slice into a STAGES-deep ring and wait for it to land; four
+//     consumer waves only read fragments (ds_read) and issue MFMAs.  A
+//     producer whose DMA cannot issue yet (the CU's load path is full) stalls
+//     alone: the consumer on its SIMD keeps the matrix pipe busy, whereas a
+//     wave that does both stalls its own MFMAs behind the blocked load;
+//   * the hand-off is gfx950's workgroup barrier, once per slice (the pages'
+//     per-slot full/empty barriers have no gfx950 counterpart; a single
+//     barrier carries both directions): between barriers i and i + 1 the
+//     consumers run slice i's MFMAs from registers and read slice i + 1's
+//     fragments, while the producers refill slot i % STAGES (slice i was read
+//     before barrier i; slice 0, read after barrier 0, has a barrier of its
+//     own) with slice i + STAGES and wait until slice i + 2 has landed, so
+//     STAGES - 2 slices of DMA stay in flight at every barrier;
+//   * every wave of a kernel gets the same register allocation, so the tile
+//     is sized for consumers of at most 256 registers: 256 x 128 or
+//     128 x 256 with 2 x 2 consumer waves of 128 x 64 or 64 x 128 (128
+//     accumulators per lane), eight waves in all, one producer and one
+//     consumer per SIMD.
+// Tails and slices past the last one are handled as in DmaTile (out-of-range
+// offsets write zeros).
+template <typename TI, typename TO, int BM_, int BN_, int BK_, int STAGES_, int CWM, int CWN, bool A_KC,
+          bool B_KC>
+struct WsTile {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
+  static constexpr int NC = CWM * CWN, NP = 4, NW = NC + NP, NT = 64 * NW;
+  static constexpr int ES = sizeof(TI);
+  using OA = DmaOperand<BM, BK, A_KC, NP, ES>;
+  using OB = DmaOperand<BN, BK, B_KC, NP, ES>;
+  static constexpr int A_BYTES = OA::BYTES, B_BYTES = OB::BYTES;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int A_INST = OA::INST, B_INST = OB::INST;
+  static constexpr int LOADS = A_INST + B_INST;  // DMA instructions per producer wave per slice
+  static constexpr int WTM = BM / CWM, WTN = BN / CWN;
+  static constexpr int MI = WTM / 16, NJ = WTN / 16;
+  static constexpr int RD_B = NJ * OB::READS, RD_A = MI * OA::READS, RD = RD_A + RD_B;
+  static constexpr int MFMAS = MI * NJ;
+  static constexpr int PO = (RD + MFMAS - 1) / MFMAS;  // fragment reads after each MFMA
+  static_assert(ES == 2 && BK * ES == 64, "16-bit inputs, one k-step (32 k) per slice");
+  static_assert(NC == 4, "four consumer waves, one per SIMD next to one producer");
+  static_assert(STAGES >= 3 && STAGES * STAGE_BYTES <= 160 * 1024, "ring depth and LDS budget");
+  static_assert(LOADS * (STAGES - 2) < 64, "vmcnt range");
+
+  static __device__ __forceinline__ void run(const GemmParams &p) {
+    __shared__ __attribute__((aligned(1024))) char lds[STAGES * STAGE_BYTES];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int tm, tn, kb, K;
+    work_coords(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, p.splits, p.K, p.k_chunk, tm, tn, kb, K);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int nk = (K + BK - 1) / BK;  // >= 1: K == 0 never reaches a tile kernel
+
+    if (wave >= NC) {  // ---------------------------------------- producer
+      const int pw = wave - NC;
+      const char *Ab = static_cast<const char *>(p.A) +
+                       (A_KC ? (int64_t)m0 * p.lda + kb : (int64_t)kb * p.lda + m0) * ES;
+      const char *Bb = static_cast<const char *>(p.B) +
+                       (B_KC ? (int64_t)n0 * p.ldb + kb : (int64_t)kb * p.ldb + n0) * ES;
+      const int64_t a_step = (A_KC ? BK : (int64_t)BK * p.lda) * ES;
+      const int64_t b_step = (B_KC ? BK : (int64_t)BK * p.ldb) * ES;
+      const uint32_t lda_b = (uint32_t)(p.lda * ES), ldb_b = (uint32_t)(p.ldb * ES);
+      const int rva = p.M - m0, rvb = p.N - n0;
+      auto issue = [&](int kt) {  // slice kt into slot kt % STAGES; past the last slice: zeros, no reads
+        char *st = lds + (kt % STAGES) * STAGE_BYTES;
+        const int kv = K - kt * BK;
+#pragma unroll
+        for (int u = 0; u < A_INST; ++u) OA::dma(make_rsrc(Ab + kt * a_step), lda_b, rva, kv, st, pw, lane, u);
+#pragma unroll
+        for (int u = 0; u < B_INST; ++u)
+          OB::dma(make_rsrc(Bb + kt * b_step), ldb_b, rvb, kv, st + A_BYTES, pw, lane, u);
+      };
+#pragma unroll
+      for (int s = 0; s < STAGES; ++s) issue(s);
+      wait_vmcnt<LOADS * (STAGES - 2)>();  // slices 0 and 1 have landed
+      lds_barrier();                       // barrier 0
+      lds_barrier();                       // the consumers hold slice 0's fragments: slot 0 may be refilled
+      for (int i = 0; i < nk; ++i) {
+        issue(i + STAGES);                   // slot i % STAGES: slice i was read before barrier i
+        wait_vmcnt<LOADS * (STAGES - 2)>();  // slice i + 2 has landed
+        lds_barrier();                       // barrier i + 1
+      }
+      wait_vmcnt<0>();  // the trailing (all out-of-range) DMA has landed before the LDS is released
+      return;
+    }
+
+    // ----------------------------------------------------------- consumer
+    const int wm = wave / CWN, wn = wave % CWN;
+    f32x4 acc[MI][NJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    typename OA::template Frag<MI, 1> fra;
+    typename OB::template Frag<NJ, 1> frb;
+    fra.init(lane, wm * MI);
+    frb.init(lane, wn * NJ);
+    auto read_op = [&](const char *st, int t, u32x4 (&fa)[MI], u32x4 (&fb)[NJ]) {
+      if (t < RD_B) frb.read(st + A_BYTES, t / OB::READS, 0, t % OB::READS, fb[t / OB::READS]);
+      else fra.read(st, (t - RD_B) / OA::READS, 0, (t - RD_B) % OA::READS, fa[(t - RD_B) / OA::READS]);
+    };
+    u32x4 fa[2][MI], fb[2][NJ];
+    lds_barrier();  // barrier 0: slices 0 and 1 are in LDS
+#pragma unroll
+    for (int t = 0; t < RD; ++t) read_op(lds, t, fa[0], fb[0]);
+    wait_lgkm0_fenced();
+    lds_barrier();  // slice 0's fragments are in registers: the producers may refill slot 0
+    for (int i = 0; i < nk; i += 2) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {  // two slices per trip keep the fragment buffers static
+        const int k = i + h;
+        const char *nx = lds + ((k + 1) % STAGES) * STAGE_BYTES;
+        const bool more = k + 1 < nk;
+#pragma unroll
+        for (int t = 0; t < MFMAS; ++t) {
+          const int ii = t / NJ, jj = t % NJ;
+          Mfma<TI>::step(acc[ii][jj], fb[h][jj], fa[h][ii]);
+#pragma unroll
+          for (int o = t * PO; o < (t + 1) * PO; ++o)
+            if (o < RD && more) read_op(nx, o, fa[h ^ 1], fb[h ^ 1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        wait_lgkm0_fenced();  // slice k + 1's fragments are in registers; slot k % STAGES is no longer read
+        lds_barrier();        // barrier k + 1
+        if (!more) break;
+      }
+    }
+    if (p.splits > 1)
+      GemmEpilogue<float, MI, NJ>::store(partial_params(p, kb), acc, m0 + wm * WTM, n0 + wn * WTN, lane);
+    else
+      GemmEpilogue<TO, MI, NJ>::store(p, acc, m0 + wm * WTM, n0 + wn * WTN, lane);
   }
 };
 

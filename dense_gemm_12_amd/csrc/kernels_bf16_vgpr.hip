@@ -22,6 +22,9 @@ const KernelEntry *entries_bf16_vgpr(int *n) {
       make_entry<__bf16, __bf16, 128, 128, 64, 2, 2, false, false>("elemAB_bf16_128x128x64_w2x2"),
       make_dma_entry<__bf16, __bf16, 256, 256, 32, 4, 2, 4, true>("dma_bf16_256x256x32_s4_w2x4_pp"),
       make_dma_entry<__bf16, __bf16, 256, 256, 32, 4, 4, 2, true>("dma_bf16_256x256x32_s4_w4x2_pp"),
+      make_ws_entry<__bf16, __bf16, 256, 128, 32, 6, 2, 2>("ws_bf16_256x128x32_s6_w2x2"),
+      make_ws_entry<__bf16, __bf16, 128, 256, 32, 6, 2, 2>("ws_bf16_128x256x32_s6_w2x2"),
+      make_ws_entry<__bf16, __bf16, 256, 128, 32, 4, 2, 2>("ws_bf16_256x128x32_s4_w2x2"),
   };
   *n = (int)(sizeof(table) / sizeof(table[0]));
   return table;

@@ -103,6 +103,38 @@ KernelEntry make_dma_entry(const char *name) {
   return e;
 }
 
+template <typename TI, typename TO, int BM, int BN, int BK, int ST, int CWM, int CWN>
+struct WsLayoutSet {
+  template <bool AKC, bool BKC>
+  using T = WsTile<TI, TO, BM, BN, BK, ST, CWM, CWN, AKC, BKC>;
+  static void fill(LaunchFn (&f)[2][2]) {
+    f[0][0] = &launch_dma_tile<T<false, false>>;
+    f[0][1] = &launch_dma_tile<T<false, true>>;
+    f[1][0] = &launch_dma_tile<T<true, false>>;
+    f[1][1] = &launch_dma_tile<T<true, true>>;
+  }
+};
+
+// Producer/consumer configurations (16-bit inputs, 16-byte-loadable operands).
+template <typename TI, typename TO16, int BM, int BN, int BK, int ST, int CWM, int CWN>
+KernelEntry make_ws_entry(const char *name) {
+  KernelEntry e{};
+  e.name = name;
+  e.bm = BM;
+  e.bn = BN;
+  e.bk = BK;
+  e.a_vec = true;
+  e.b_vec = true;
+  e.kind = 1;
+  WsLayoutSet<TI, float, BM, BN, BK, ST, CWM, CWN>::fill(e.fn[1]);
+  WsLayoutSet<TI, TO16, BM, BN, BK, ST, CWM, CWN>::fill(e.fn[0]);
+  using Rep = typename WsLayoutSet<TI, float, BM, BN, BK, ST, CWM, CWN>::template T<true, true>;
+  e.threads = Rep::NT;
+  e.lds_bytes = ST * Rep::STAGE_BYTES;
+  e.occupancy = &occupancy_dma_tile<Rep>;
+  return e;
+}
+
 template <class Tile>
 hipError_t launch_valu_tile(const GemmParams &p, hipStream_t s) {
   hipLaunchKernelGGL(gemm_valu_kernel<Tile>, dim3(p.tiles_m * p.tiles_n * p.splits), dim3(Tile::NT), 0, s,

@@ -205,6 +205,9 @@ size_t mg_split16_workspace_size(int64_t M, int64_t N, int64_t K);
  * <staging>_<type>_<BM>x<BN>x<BK>[_s<stages>][_w<waves along M>x<waves along N>][_pp],
  * e.g. "dma_f16_256x256x64_s2_w2x4":
  *   dma     direct-to-LDS loads (both operands must be 16-byte loadable);
+ *   ws      direct-to-LDS loads issued by four dedicated producer waves for
+ *           the consumer waves (_w gives the consumer waves) that only read
+ *           fragments and issue matrix instructions (same requirement);
  *   mfma    16-byte loads staged through registers (same requirement);
  *   elemA / elemB / elemAB   element loads for A / B / both (any alignment);
  *   valu    fp32 on the vector ALUs (fp32 C only);

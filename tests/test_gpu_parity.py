@@ -89,6 +89,30 @@ def test_every_config_every_layout_integer_bit_exact(in_dtype):
                     assert_bit_exact(got, ref, c_dtype, what)
 
 
+@pytest.mark.parametrize("in_dtype", ["f16", "bf16"])
+def test_every_16bit_config_long_k_integer_bit_exact(in_dtype):
+    """Forced 16-bit configurations with K from one slice to many trips
+    around the deepest LDS ring (odd and even slice counts, a ragged last
+    slice), in the two headline layouts (TN with 16-bit C, NN with fp32 C and
+    beta = 1) and their mirror images."""
+    import dense_gemm_12_amd as mg
+    n = mg.num_configs(in_dtype)
+    cases = [(False, True, in_dtype), (False, False, "f32"), (True, True, in_dtype), (True, False, "f32")]
+    for (ta, tb, c_dtype) in cases:
+        for K in (32, 64, 96, 544, 1000):
+            M, N = 264, 392
+            A, B, C = make(M, N, K, ta, tb, in_dtype, c_dtype, "int2", 31 + K)
+            ref = oracle_full(A, B, C, alpha=1.0, beta=1.0, ta=ta, tb=tb, in_dtype=in_dtype, c_dtype=c_dtype)
+            for cfg in range(n):
+                name = mg.config_name(in_dtype, cfg)
+                if not name.startswith(("dma", "ws")):
+                    continue
+                what = f"{name} ta={ta} tb={tb} c={c_dtype} {M}x{N}x{K}"
+                log("case " + what)
+                got = run_gpu(A, B, C, alpha=1.0, beta=1.0, ta=ta, tb=tb, c_dtype=c_dtype, config=cfg)
+                assert_bit_exact(got, ref, c_dtype, what)
+
+
 def test_forced_vector_config_refuses_unaligned_problem():
     import dense_gemm_12_amd as mg
     A, B, C = make(64, 70, 64, False, False, "f16", "f16", "int2", 12)
