@@ -190,7 +190,7 @@ struct DmaOperand {
 };
 
 template <typename TI, typename TO, int BM_, int BN_, int BK_, int STAGES_, int WAVES_M, int WAVES_N,
-          bool A_KC, bool B_KC, bool PINGPONG = false>
+          bool A_KC, bool B_KC, bool PINGPONG = false, bool STREAMK = false>
 struct DmaTile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
   static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
@@ -218,15 +218,173 @@ struct DmaTile {
   static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS budget");
   static_assert(LOADS_PER_SLICE * (STAGES - 1) < 64, "vmcnt range");
 
+  // LDS: the slice ring, and for stream-K one more word (the "last
+  // contributor" flag) in the same array.  A second __shared__ object makes
+  // the compiler put a vmcnt(0) wait in front of ring reads that it can no
+  // longer tell apart from the DMA in flight.
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES + (STREAMK ? 16 : 0);
+
   static __device__ __forceinline__ void run(const GemmParams &p) {
-    __shared__ __attribute__((aligned(1024))) char lds[STAGES * STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    f32x4 acc[MI][NJ];
+    if constexpr (STREAMK) {
+      stream_k(p, lds, wave, lane, wm, wn, acc);
+    } else {
+      int tm, tn, kb, K;
+      work_coords(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, p.splits, p.K, p.k_chunk, tm, tn, kb, K);
+      const int m0 = tm * BM, n0 = tn * BN;
+      compute(p, lds, m0, n0, kb, K, wave, lane, wm, wn, acc);
+      if (p.splits > 1)
+        GemmEpilogue<float, MI, NJ, A_Q, B_Q>::store(partial_params(p, kb), acc, m0 + wm * WTM,
+                                                     n0 + wn * WTN, lane);
+      else
+        GemmEpilogue<TO, MI, NJ, A_Q, B_Q>::store(p, acc, m0 + wm * WTM, n0 + wn * WTN, lane);
+    }
+  }
 
-    int tm, tn, kb, K;
-    work_coords(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, p.splits, p.K, p.k_chunk, tm, tn, kb, K);
-    const int m0 = tm * BM, n0 = tn * BN;
+  // Stream-K schedule ("Stream-K: Work-centric Parallel Decomposition for
+  // Dense Matrix-Matrix Multiplication on the GPU", Osama, Merrill, Cecka,
+  // Garland and Owens, 2023), the persistent form of the split-K idea the
+  // worklog's Kernel 10 section sees cuBLAS use: the grid is p.sk_grid
+  // workgroups of one round of the chip, after p.sk_dp_tiles workgroups
+  // that each take one whole tile in the plain grid's order (all rounds but
+  // the last one or two: these are dispatched first, and the hardware
+  // balances them over the CUs as in the plain grid).  The slice iterations
+  // of the remaining tiles are cut into p.sk_grid equal contiguous ranges,
+  // and each of the last p.sk_grid workgroups runs its range tile by tile.
+  // A tile covered whole by one
+  // workgroup is finished there; a tile whose slices are shared by several
+  // workgroups ("contributors", ordered by k) is finished by the one that
+  // completes last, with no waiting:
+  //   every contributor stores its fp32 sums to its own workspace slot (2w
+  //   for the tile its range starts in, 2w + 1 for the tile it ends in, in
+  //   the accumulator register layout, 1 KiB per store instruction) with
+  //   device-coherent stores, waits until they are acknowledged and
+  //   increments the tile's counter; the contributor that sees the count
+  //   reach the number of contributors reads every slot back with
+  //   device-coherent loads, adds them in contributor order (so the result
+  //   does not depend on which one finished last) and runs the alpha/beta
+  //   epilogue.
+  // Ranges of different workgroups end at different points of their tiles,
+  // so epilogues are spread over the run instead of coming in one burst per
+  // round, and no round is left partly empty.  The counters (p.sk_cnt, one
+  // per tile) must be zero at launch; tiles x sk_ipt < 2^31 (host-checked).
+  static __device__ __forceinline__ int sk_start(const GemmParams &p, int total, int w) {
+    return (int)((int64_t)total * w / p.sk_grid);
+  }
+  static __device__ __forceinline__ int sk_owner(const GemmParams &p, int total, int it) {
+    int w = (int)((int64_t)it * p.sk_grid / total);  // start(w) <= it up to rounding; step to the exact owner
+    while (w + 1 < p.sk_grid && sk_start(p, total, w + 1) <= it) ++w;
+    while (w > 0 && sk_start(p, total, w) > it) --w;
+    return w;
+  }
+
+  static __device__ __forceinline__ void stream_k(const GemmParams &p, char *lds, int wave, int lane, int wm,
+                                                  int wn, f32x4 (&acc)[MI][NJ]) {
+    int &s_last = *reinterpret_cast<int *>(lds + STAGES * STAGE_BYTES);
+    const int ipt = p.sk_ipt, G = p.sk_grid;
+    const int dp = p.sk_dp_tiles;  // leading whole tiles, one workgroup each, dispatched first
+    const int total = (p.tiles_m * p.tiles_n - dp) * ipt;  // slice iterations of the stream-K tail
+    const int b = blockIdx.x;
+    // tail workgroups: logical index w, each XCD gets a contiguous block of ranges
+    const int w = b < dp ? 0 : remap_xcd(b - dp, G);
+    int it = b < dp ? 0 : sk_start(p, total, w);
+    const int it1 = b < dp ? 0 : sk_start(p, total, w + 1);
+    constexpr int TILE_F4 = BM * BN / 4;  // f32x4 per partial slot
+    for (bool whole = b < dp; whole || it < it1;) {
+      int t, kbeg, kend;
+      if (whole) {  // a data-parallel workgroup: one tile, whole, in the plain grid's order
+        t = remap_xcd(b, dp);
+        kbeg = 0;
+        kend = ipt;
+        whole = false;
+      } else {  // the stream-K tail: this workgroup's slice range, tile by tile
+        const int tt = it / ipt;
+        kbeg = it - tt * ipt;
+        kend = min(ipt, kbeg + (it1 - it));
+        t = dp + tt;
+        it += kend - kbeg;
+      }
+      // Per-lane values are recomputed in every unit: made opaque here, they
+      // are not hoisted out of this loop to stay live (and spill) across the
+      // whole k-loop.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      int tm, tn;
+      tile_coords(t, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+      const int m0 = tm * BM, n0 = tn * BN;
+      const int kb = kbeg * BK;
+      __syncthreads();  // every wave is done with the previous unit's LDS before the ring refills
+      compute(p, lds, m0, n0, kb, min(p.K - kb, (kend - kbeg) * BK), wave, ln, wm, wn, acc);
+      if (kbeg != 0 || kend != ipt) {
+        const int tt = t - dp;
+        const int wf = sk_owner(p, total, tt * ipt);
+        const int nc = sk_owner(p, total, (tt + 1) * ipt - 1) - wf + 1;  // contributors
+        // Partial sums move with device-scope buffer accesses (cache policy
+        // SC1): a store is acknowledged once it is coherent for every XCD,
+        // and a load is served coherently, bypassing stale copies in this
+        // CU's L1 and this XCD's L2.  So no L2-wide write-back or invalidate
+        // (the agent-scope fences) is needed, which would also throw away
+        // the operand tiles the XCD's other workgroups are reading.
+        constexpr int kDeviceScope = 16;  // SC1
+        const __amdgpu_buffer_rsrc_t ws = make_rsrc(p.ws);
+        // byte offset of this lane's f32x4 of accumulator block (i, j) in the
+        // slot of contributor v for tile t: 2v if tile t is where v's range
+        // starts, else 2v + 1
+        const uint32_t lane_off = (uint32_t)(wave * MI * NJ * 64 + ln) * 16;
+        auto slot = [&](int v) -> uint32_t {
+          const int first = sk_start(p, total, v) / ipt == tt ? 0 : 1;
+          return (uint32_t)(2 * v + first) * (TILE_F4 * 16) + lane_off;
+        };
+        {
+          const uint32_t mine = slot(w);
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), ws,
+                                                     mine + (i * NJ + j) * 1024, 0, kDeviceScope);
+        }
+        wait_vmcnt<0>();  // this wave's sums are coherent device-wide
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          const int old = __hip_atomic_fetch_add(p.sk_cnt + t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          s_last = old == nc - 1;
+        }
+        __syncthreads();
+        if (!s_last) continue;
+        // The last contributor: every slot, its own included, in contributor order.
+        {
+          const uint32_t first = slot(wf);
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+              acc[i][j] = __builtin_bit_cast(
+                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(ws, first + (i * NJ + j) * 1024, 0, kDeviceScope));
+        }
+        for (int q = 1; q < nc; ++q) {
+          const uint32_t sq = slot(wf + q);
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+              acc[i][j] += __builtin_bit_cast(
+                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(ws, sq + (i * NJ + j) * 1024, 0, kDeviceScope));
+        }
+      }
+      GemmEpilogue<TO, MI, NJ, A_Q, B_Q>::store(p, acc, m0 + wm * WTM, n0 + wn * WTN, ln);
+    }
+  }
+
+  // The k-loop of one work unit: the tile at (m0, n0), k in [kb, kb + K).
+  // Leaves the unit's sums in acc; on return every DMA and LDS read of the
+  // unit has completed (the LDS ring may be refilled after a barrier).
+  static __device__ __forceinline__ void compute(const GemmParams &p, char *lds, int m0, int n0, int kb, int K,
+                                                 int wave, int lane, int wm, int wn, f32x4 (&acc)[MI][NJ]) {
     // Slice origins advance by BK along k: BK elements for a k-contiguous
     // operand, BK rows for a k-major one.
     const char *Ab = static_cast<const char *>(p.A) +
@@ -252,7 +410,6 @@ struct DmaTile {
       for (int u = 0; u < LOADS_PER_SLICE; ++u) dma_op(kt, u);
     };
 
-    f32x4 acc[MI][NJ];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -466,11 +623,6 @@ struct DmaTile {
     // not exist in flight; their registers are dead, and the epilogue may
     // reuse them for addresses, so those reads must land first.
     wait_lgkm0_fenced();
-    if (p.splits > 1)
-      GemmEpilogue<float, MI, NJ, A_Q, B_Q>::store(partial_params(p, kb), acc, m0 + wm * WTM, n0 + wn * WTN,
-                                                   lane);
-    else
-      GemmEpilogue<TO, MI, NJ, A_Q, B_Q>::store(p, acc, m0 + wm * WTM, n0 + wn * WTN, lane);
   }
 };
 

@@ -318,6 +318,13 @@ __global__ void __launch_bounds__(256) pack_rows_kernel(const void *src, int64_t
   }
 }
 
+// Stream-K arrival counters to zero before the tile kernel (a kernel, not a
+// memset, so the call can be captured in a HIP graph).
+template <int Unused = 0>
+__global__ void __launch_bounds__(256) zero_ints_kernel(int *p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
 // Split-K reduction: C = alpha * (P_0 + P_1 + ... + P_{S-1}) + beta * C with
 // the partials summed in split order, so the result does not depend on
 // which split finished first; one rounding to the C type, and beta == 0

@@ -29,6 +29,15 @@ struct GemmParams {
   // 2^-(row_exp[m] + col_exp[n]) before alpha and beta are applied.
   const int *row_exp;
   const int *col_exp;
+  // Stream-K (configurations marked sk): sk_dp_tiles + sk_grid workgroups;
+  // the first sk_dp_tiles each take one whole tile, the last sk_grid share
+  // the slice iterations of the other tiles (sk_ipt per tile) in equal
+  // contiguous ranges; partial tiles go to ws (2 * sk_grid slots of BM * BN
+  // floats) and sk_cnt holds one zero-initialised arrival counter per tile.
+  int sk_grid;
+  int sk_ipt;
+  int sk_dp_tiles;  // leading tiles dealt whole (a multiple of sk_grid); the rest is split
+  int *sk_cnt;
 };
 
 typedef hipError_t (*LaunchFn)(const GemmParams &, hipStream_t);
@@ -50,6 +59,7 @@ struct KernelEntry {
   int threads;          // workgroup size
   int lds_bytes;        // static LDS per workgroup
   OccupancyFn occupancy;  // asked of the HIP runtime for one representative layout
+  bool sk;              // stream-K schedule: needs a workspace (gemm_ex), never picked by the cost model
 };
 
 const KernelEntry *entries_f32(int *n);
@@ -60,6 +70,8 @@ const KernelEntry *entries_bf16_vgpr(int *n);
 
 LaunchFn scale_launcher(int c_dtype);   // 0 = f32, 1 = f16, 2 = bf16
 LaunchFn reduce_launcher(int c_dtype);  // split-K partial sums -> C, same codes
+// Zeroes n ints (stream-K arrival counters) on the stream.
+hipError_t launch_zero_ints(int *p, int n, hipStream_t s);
 // Copies a rows x cols operand (es-byte elements) into a zero-padded buffer
 // with a 16-byte-multiple row pitch.
 hipError_t launch_pack(int es, const void *src, int64_t ld, int64_t rows, int64_t cols, void *dst,

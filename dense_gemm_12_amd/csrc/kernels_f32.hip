@@ -72,6 +72,13 @@ hipError_t launch_pack(int es, const void *src, int64_t ld, int64_t rows, int64_
   return hipGetLastError();
 }
 
+hipError_t launch_zero_ints(int *p, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+  hipLaunchKernelGGL(zero_ints_kernel<0>, dim3(blocks), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
 LaunchFn scale_launcher(int c_dtype) {
   switch (c_dtype) {
     case 0: return &launch_scale<float>;

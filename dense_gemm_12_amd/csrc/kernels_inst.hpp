@@ -66,15 +66,15 @@ KernelEntry make_entry(const char *name) {
 
 template <class Tile>
 hipError_t launch_dma_tile(const GemmParams &p, hipStream_t s) {
-  hipLaunchKernelGGL(gemm_dma_kernel<Tile>, dim3(p.tiles_m * p.tiles_n * p.splits), dim3(Tile::NT), 0, s,
-                     p);
+  const int grid = p.sk_grid > 0 ? p.sk_dp_tiles + p.sk_grid : p.tiles_m * p.tiles_n * p.splits;
+  hipLaunchKernelGGL(gemm_dma_kernel<Tile>, dim3(grid), dim3(Tile::NT), 0, s, p);
   return hipGetLastError();
 }
 
-template <typename TI, typename TO, int BM, int BN, int BK, int ST, int WM, int WN, bool PP>
+template <typename TI, typename TO, int BM, int BN, int BK, int ST, int WM, int WN, bool PP, bool SK = false>
 struct DmaLayoutSet {
   template <bool AKC, bool BKC>
-  using T = DmaTile<TI, TO, BM, BN, BK, ST, WM, WN, AKC, BKC, PP>;
+  using T = DmaTile<TI, TO, BM, BN, BK, ST, WM, WN, AKC, BKC, PP, SK>;
   static void fill(LaunchFn (&f)[2][2]) {
     f[0][0] = &launch_dma_tile<T<false, false>>;
     f[0][1] = &launch_dma_tile<T<false, true>>;
@@ -84,7 +84,8 @@ struct DmaLayoutSet {
 };
 
 // Direct-to-LDS configurations (16-bit inputs, 16-byte-loadable operands).
-template <typename TI, typename TO16, int BM, int BN, int BK, int ST, int WM, int WN, bool PP = false>
+template <typename TI, typename TO16, int BM, int BN, int BK, int ST, int WM, int WN, bool PP = false,
+          bool SK = false>
 KernelEntry make_dma_entry(const char *name) {
   KernelEntry e{};
   e.name = name;
@@ -94,9 +95,10 @@ KernelEntry make_dma_entry(const char *name) {
   e.a_vec = true;
   e.b_vec = true;
   e.kind = 1;
-  DmaLayoutSet<TI, float, BM, BN, BK, ST, WM, WN, PP>::fill(e.fn[1]);
-  DmaLayoutSet<TI, TO16, BM, BN, BK, ST, WM, WN, PP>::fill(e.fn[0]);
-  using Rep = typename DmaLayoutSet<TI, float, BM, BN, BK, ST, WM, WN, PP>::template T<true, true>;
+  e.sk = SK;
+  DmaLayoutSet<TI, float, BM, BN, BK, ST, WM, WN, PP, SK>::fill(e.fn[1]);
+  DmaLayoutSet<TI, TO16, BM, BN, BK, ST, WM, WN, PP, SK>::fill(e.fn[0]);
+  using Rep = typename DmaLayoutSet<TI, float, BM, BN, BK, ST, WM, WN, PP, SK>::template T<true, true>;
   e.threads = Rep::NT;
   e.lds_bytes = ST * Rep::STAGE_BYTES;
   e.occupancy = &occupancy_dma_tile<Rep>;

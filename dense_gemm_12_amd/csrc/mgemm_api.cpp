@@ -223,7 +223,7 @@ int model_config(const Table &t, const Problem &p, double *est = nullptr) {
   int best = -1;
   double best_t = 0.0;
   for (int i = 0; i < n; ++i) {
-    if (!usable(e[i], p) || e[i].kind == 2) continue;
+    if (!usable(e[i], p) || e[i].kind == 2 || e[i].sk) continue;
     const double ti = est_time(t, p, i, e[i]);
     if (best < 0 || ti < best_t * (1.0 - 1e-9) ||
         (ti <= best_t * (1.0 + 1e-9) && (int64_t)e[i].bm * e[i].bn > (int64_t)e[best].bm * e[best].bn)) {
@@ -289,6 +289,8 @@ Plan plan(const Problem &p) {
     // a rule naming an element-load variant was tuned on operands 16-byte
     // loads could not read; these can be, so the rule does not apply
     if (c >= 0 && !usable(e[c], p)) c = -1;
+    // stream-K needs a workspace: only calls that bring one may use it
+    if (c >= 0 && e[c].sk && !p.ws_path) c = -1;
     pl.config = c >= 0 ? c : model_config(*t, p);
   } else {
     pl.config = elem_config(p.in_type, pl.a_vec, pl.b_vec);
@@ -348,6 +350,33 @@ static Pack pack_shape(const Problem &p, bool is_a) {
   if (k.pitch > kMaxLd || k.rows <= 0 || k.cols <= 0) return Pack{0, 0, 0, 0};
   k.bytes = ((size_t)k.rows * k.pitch * es + 255) / 256 * 256;
   return k;
+}
+
+// Stream-K shape of configuration cfg on problem p: one round of the chip
+// (256 CUs x the configuration's workgroups per CU, at most one workgroup
+// per slice iteration) and the workspace it needs: 2 partial-tile slots of
+// BM x BN floats per workgroup, then one arrival counter per tile.
+struct SkShape {
+  int grid, ipt, dp_tiles;
+  int64_t tiles, total;
+  size_t slots_bytes, bytes;
+};
+
+static SkShape sk_shape(const Table &t, const Problem &p, int cfg, const KernelEntry &k) {
+  SkShape sh{};
+  sh.tiles = tiles_for(p.M, p.N, k.bm, k.bn);
+  sh.ipt = (int)((p.K + k.bk - 1) / k.bk);
+  sh.total = sh.tiles * sh.ipt;
+  int64_t g = kFillWorkgroups * (int64_t)occupancy(t, p.in_type, cfg, k);
+  if (g > sh.total) g = sh.total;
+  sh.grid = (int)(g < 1 ? 1 : g);
+  // all rounds but the last two are data-parallel; the last one to two
+  // rounds' worth of tiles is shared in slice ranges
+  const int64_t rounds = sh.tiles / sh.grid;
+  sh.dp_tiles = (int)(rounds >= 2 ? (rounds - 1) * sh.grid : 0);
+  sh.slots_bytes = (size_t)2 * sh.grid * k.bm * k.bn * 4;
+  sh.bytes = sh.slots_bytes + ((size_t)sh.tiles * 4 + 255) / 256 * 256;
+  return sh;
 }
 
 // Implementation shared by the entry points.  splits: 0 = planner's choice
@@ -433,6 +462,17 @@ static mg_status run(const Problem &p, int forced, int splits, void *ws, size_t 
     Plan pl = plan(p);
     int cfg = forced >= 0 ? forced : pl.config;
     if (cfg < 0) return MG_EUNSUPPORTED;
+    SkShape sk{};
+    if (e[cfg].sk) {
+      const std::shared_ptr<const Table> t = table_snapshot();
+      sk = sk_shape(*t, p, cfg, e[cfg]);
+      if (sk.total >= kMaxDim) return MG_EUNSUPPORTED;
+      if (ws == nullptr || ws_bytes < sk.bytes) {
+        if (forced >= 0) return MG_EUNSUPPORTED;
+        cfg = model_config(*t, p);  // the planner's stream-K pick without room for it
+        if (cfg < 0) return MG_EUNSUPPORTED;
+      }
+    }
     const KernelEntry &k = e[cfg];
     if ((k.a_vec && !pl.a_vec) || (k.b_vec && !pl.b_vec)) return MG_EUNSUPPORTED;
     const int ci = (p.c_type == MG_F32) ? 1 : 0, ak = p.ta == MG_N ? 1 : 0, bk = p.tb == MG_T ? 1 : 0;
@@ -440,17 +480,28 @@ static mg_status run(const Problem &p, int forced, int splits, void *ws, size_t 
     gp.tiles_m = (int)((p.M + k.bm - 1) / k.bm);
     gp.tiles_n = (int)((p.N + k.bn - 1) / k.bn);
     gp.group_m = 8;
-    int chunk = 0;
-    const int sp = split_shape(p.K, k.bk, splits == 0 ? auto_splits(p, k, (int64_t)ws_bytes, pl.splits) : splits,
-                               &chunk);
-    if ((int64_t)gp.tiles_m * gp.tiles_n * sp >= kMaxDim) return MG_EUNSUPPORTED;
-    gp.splits = sp;
-    gp.k_chunk = chunk;
-    gp.ws = static_cast<float *>(ws);
     const int c_is_f32 = (p.c_type == MG_F32) ? 1 : 0;
     const int a_kc = p.ta == MG_N ? 1 : 0, b_kc = p.tb == MG_T ? 1 : 0;
-    err = k.fn[c_is_f32][a_kc][b_kc](gp, stream);
-    if (err == hipSuccess && sp > 1) err = mg::reduce_launcher(c_idx)(gp, stream);
+    if (k.sk) {
+      // stream-K: partial-tile slots, then the zeroed arrival counters
+      gp.ws = static_cast<float *>(ws);
+      gp.sk_cnt = reinterpret_cast<int *>(static_cast<char *>(ws) + sk.slots_bytes);
+      gp.sk_grid = sk.grid;
+      gp.sk_ipt = sk.ipt;
+      gp.sk_dp_tiles = sk.dp_tiles;
+      err = mg::launch_zero_ints(gp.sk_cnt, (int)sk.tiles, stream);
+      if (err == hipSuccess) err = k.fn[c_is_f32][a_kc][b_kc](gp, stream);
+    } else {
+      int chunk = 0;
+      const int sp = split_shape(p.K, k.bk,
+                                 splits == 0 ? auto_splits(p, k, (int64_t)ws_bytes, pl.splits) : splits, &chunk);
+      if ((int64_t)gp.tiles_m * gp.tiles_n * sp >= kMaxDim) return MG_EUNSUPPORTED;
+      gp.splits = sp;
+      gp.k_chunk = chunk;
+      gp.ws = static_cast<float *>(ws);
+      err = k.fn[c_is_f32][a_kc][b_kc](gp, stream);
+      if (err == hipSuccess && sp > 1) err = mg::reduce_launcher(c_idx)(gp, stream);
+    }
   }
   if (err != hipSuccess) {
     g_last_hip_error = (int)err;
@@ -619,6 +670,7 @@ size_t mg_workspace_size(mg_dtype in_type, mg_dtype c_type, mg_op ta, mg_op tb, 
   if (pl.config < 0) return packed;
   int n = 0;
   const KernelEntry &k = entries(p.in_type, &n)[pl.config];
+  if (k.sk) return packed + sk_shape(*table_snapshot(), p, pl.config, k).bytes;
   int chunk = 0;
   const int sp = split_shape(K, k.bk, auto_splits(p, k, INT64_MAX, pl.splits), &chunk);
   return packed + (sp > 1 ? (size_t)sp * (size_t)M * (size_t)N * 4 : 0);

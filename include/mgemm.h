@@ -212,7 +212,15 @@ size_t mg_split16_workspace_size(int64_t M, int64_t N, int64_t K);
  *   elemA / elemB / elemAB   element loads for A / B / both (any alignment);
  *   valu    fp32 on the vector ALUs (fp32 C only);
  *   _pp     the ping-pong schedule (two wave groups alternating between
- *           matrix instructions and memory instructions). */
+ *           matrix instructions and memory instructions);
+ *   _sk     the stream-K schedule: one round of persistent workgroups share
+ *           the problem's slice iterations in equal ranges, and a tile split
+ *           between workgroups is finished by the last one to reach it, from
+ *           fp32 partials in the workspace, summed in k order (deterministic).
+ *           These run only through gemm_ex with a workspace of at least
+ *           2 x 256 x BM x BN x 4 bytes plus 4 bytes per tile (a smaller one:
+ *           MG_EUNSUPPORTED when forced; the planner then takes another
+ *           configuration). */
 int mg_num_configs(mg_dtype in_type);
 const char *mg_config_name(mg_dtype in_type, int config);
 

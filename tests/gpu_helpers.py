@@ -32,6 +32,9 @@ def stored_shapes(M, N, K, ta, tb):
 
 
 GUARD = 256  # bytes after a split-K workspace that the library must not touch
+# Workspace large enough for any stream-K configuration (2 partial-tile slots
+# of 256 x 256 floats per workgroup of one 256-CU round, plus tile counters).
+SK_WS_BYTES = 2 * 256 * 256 * 256 * 4 + (1 << 20)
 
 
 def run_gpu(A, B, Cin, *, alpha, beta, ta, tb, c_dtype, config=-1, ldc=None, stream=None,

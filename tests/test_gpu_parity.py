@@ -12,8 +12,8 @@ import torch
 
 import gemm_inputs as gi
 import oracle
-from gpu_helpers import (assert_bit_exact, assert_within, log, oracle_full, out_as_f64, run_gpu,
-                         stored_shapes)
+from gpu_helpers import (SK_WS_BYTES, assert_bit_exact, assert_within, log, oracle_full, out_as_f64,
+                         run_gpu, stored_shapes)
 
 pytestmark = pytest.mark.gpu
 
@@ -84,8 +84,10 @@ def test_every_config_every_layout_integer_bit_exact(in_dtype):
                         continue
                     what = f"{name} ta={ta} tb={tb} c={c_dtype} {M}x{N}x{K}"
                     log("case " + what)
+                    # stream-K configurations run only with a workspace (through gemm_ex)
+                    ws = SK_WS_BYTES if name.endswith("_sk") else None
                     got = run_gpu(A, B, C, alpha=1.5, beta=0.5, ta=ta, tb=tb, c_dtype=c_dtype,
-                                  config=cfg)
+                                  config=cfg, workspace_bytes=ws)
                     assert_bit_exact(got, ref, c_dtype, what)
 
 
@@ -109,7 +111,9 @@ def test_every_16bit_config_long_k_integer_bit_exact(in_dtype):
                     continue
                 what = f"{name} ta={ta} tb={tb} c={c_dtype} {M}x{N}x{K}"
                 log("case " + what)
-                got = run_gpu(A, B, C, alpha=1.0, beta=1.0, ta=ta, tb=tb, c_dtype=c_dtype, config=cfg)
+                ws = SK_WS_BYTES if name.endswith("_sk") else None
+                got = run_gpu(A, B, C, alpha=1.0, beta=1.0, ta=ta, tb=tb, c_dtype=c_dtype, config=cfg,
+                              workspace_bytes=ws)
                 assert_bit_exact(got, ref, c_dtype, what)
 
 

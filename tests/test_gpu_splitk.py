@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import gemm_inputs as gi
-from gpu_helpers import (assert_bit_exact, assert_within, bits, log, oracle_full, out_as_f64,
+from gpu_helpers import (SK_WS_BYTES, assert_bit_exact, assert_within, bits, log, oracle_full, out_as_f64,
                          run_gpu, stored_shapes)
 
 pytestmark = pytest.mark.gpu
@@ -60,8 +60,10 @@ def test_every_config_split_integer_bit_exact(in_dtype):
             for (ta, tb) in LAYOUTS:
                 for c_dtype in C_TYPES[in_dtype]:
                     try:
+                        # stream-K configurations ignore the split count and need their own workspace
                         check(M, N, K, ta, tb, in_dtype, c_dtype, alpha=1.5, beta=0.5, dist="int2",
-                              seed=31, splits=3, config=cfg)
+                              seed=31, splits=3, config=cfg,
+                              ws_bytes=SK_WS_BYTES if name.endswith("_sk") else None)
                     except mg.MgemmError as e:
                         assert e.status == mg.MG_EUNSUPPORTED, (name, e)
                         log(f"  {name}: unsupported for this layout/alignment")

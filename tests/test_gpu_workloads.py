@@ -33,9 +33,15 @@ def _check_workload(name, integer_twin):
     what = f"{name}{' int' if integer_twin else ''}"
     log(f"workload {what}: generating inputs")
     A, B, C = gi.workload_inputs(name, integer_twin)
-    log(f"workload {what}: GPU run")
+    # the benchmark's launch configuration: through gemm_ex with the
+    # planner's workspace when it asks for one (split-K, repacking, stream-K)
+    import dense_gemm_12_amd as mg
+    codes = mg.DTYPE_CODES
+    ws = mg.workspace_size(codes[w["in_dtype"]], codes[w["c_dtype"]], int(w["ta"]), int(w["tb"]), M, N, K,
+                           A.stride(0), B.stride(0))
+    log(f"workload {what}: GPU run (workspace {ws} bytes)")
     got = run_gpu(A, B, C, alpha=w["alpha"], beta=w["beta"], ta=w["ta"], tb=w["tb"],
-                  c_dtype=w["c_dtype"])
+                  c_dtype=w["c_dtype"], workspace_bytes=ws if ws else None, splits=0)
     c = w["c_dtype"]
     if M * N * K <= FULL_ORACLE_MAX_MACS:
         log(f"workload {what}: full oracle")
