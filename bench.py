@@ -27,7 +27,7 @@ cores) and reported as "fp32_via_split_fp16", outside ``value``.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
                        [--cold-steps N] [--no-clocks] [--split16-steps N]
-                       [--workload NAME ...]
+                       [--workload NAME ...] [--table] [--cpu-table]
 """
 from __future__ import annotations
 
@@ -164,6 +164,13 @@ def cpu_blocked(parts):
             "cpu": cpu_gemm.cpu_model()}
 
 
+def _mhz(v):
+    """'(2106Mhz)' -> 2106.0 (None if not a clock reading)."""
+    import re
+    m = re.search(r"(\d+(?:\.\d+)?)\s*Mhz", str(v), re.I)
+    return float(m.group(1)) if m else None
+
+
 def read_clocks():
     """GPU clocks and power from rocm-smi (None where it cannot say)."""
     try:
@@ -242,6 +249,91 @@ def workload_table(mg, torch, dev, names):
         torch.cuda.empty_cache()
 
 
+def cpu_table(mg, torch, dev, names, budget_s=60.0):
+    """Per-workload CPU baselines beside the GPU time: the oracle on the whole
+    problem when a trial slab predicts at most ``budget_s`` seconds, else on a
+    row slab scaled by M / rows (marked extrapolated; the work is linear in
+    M); the blocked CPU GEMM likewise; GPU per-launch time (warm, median of
+    three runs of back-to-back launches through the planner, as ``--table``)."""
+    import oracle
+    import cpu_gemm
+    threads = oracle.default_threads()
+    model = cpu_model()
+    codes = mg.DTYPE_CODES
+    rows_out = []
+    print(f"CPU: {model}, {threads} threads", flush=True)
+    print("| workload | GFLOP | GPU µs (warm) | oracle: rows timed | oracle s (full) | oracle GFLOP/s | "
+          "GPU speed-up vs oracle | blocked: rows timed | blocked s (full) | blocked GFLOP/s | "
+          "GPU speed-up vs blocked |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|")
+    for name in names:
+        w = gi.WORKLOADS[name]
+        A, B, C = gi.workload_inputs(name)
+        M, N, K = w["M"], w["N"], w["K"]
+        fl = flops(w)
+        # GPU: the planner's launch (through gemm_ex when it asks for a workspace)
+        Ad, Bd = A.to(dev), B.to(dev)
+        Cd = C.to(dev) if C is not None else torch.zeros((M, N), dtype=gi.DTYPES[w["c_dtype"]], device=dev)
+        wsb = mg.workspace_size(codes[w["in_dtype"]], codes[w["c_dtype"]], int(w["ta"]), int(w["tb"]), M, N, K,
+                                Ad.stride(0), Bd.stride(0))
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+        call = lambda: mg.gemm(Ad, Bd, Cd, alpha=w["alpha"], beta=w["beta"], trans_a=w["ta"], trans_b=w["tb"],
+                               workspace=ws)
+        call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        torch.cuda.synchronize()
+        reps = max(20, int(100.0 / max(e0.elapsed_time(e1), 1e-3)))
+        tr = []
+        for _ in range(3):
+            e0.record()
+            for _ in range(reps):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            tr.append(e0.elapsed_time(e1) / reps * 1e-3)
+        gpu_s = statistics.median(tr)
+        del Ad, Bd, Cd, ws
+        torch.cuda.empty_cache()
+        bits = lambda t: None if t is None else gi.as_numpy_bits(t)
+        An, Bn, Cn = bits(A), bits(B), bits(C)
+        kw = dict(a_dtype=w["in_dtype"], trans_a=w["ta"], trans_b=w["tb"], alpha=w["alpha"], beta=w["beta"],
+                  c_dtype=w["c_dtype"], M=M, N=N, K=K)
+
+        def timed(fn, r):
+            t0 = time.perf_counter()
+            fn(r)
+            return time.perf_counter() - t0
+
+        def measure(fn):
+            # trial slab, then the whole problem or a slab of about budget_s / 4
+            trial = min(M, max(threads, 16))
+            t_trial = timed(fn, trial)
+            est_full = t_trial * M / trial
+            if est_full <= budget_s:
+                return M, timed(fn, M), False
+            r = int(min(M, max(trial, M * (budget_s / 4) / est_full)))
+            return r, timed(fn, r) * M / r, True
+
+        o_rows, o_s, o_ext = measure(lambda r: oracle.gemm(An, Bn, C=Cn, rows=(0, r), threads=threads, **kw))
+        Cf = None if C is None else C.float().numpy()
+        b_rows, b_s, b_ext = measure(lambda r: cpu_gemm.gemm_rows(
+            An, Bn, in_dtype=w["in_dtype"], ta=w["ta"], tb=w["tb"], M=M, N=N, K=K, alpha=w["alpha"],
+            beta=w["beta"], Cin=Cf, rows=(0, r), threads=threads))
+        rec = {"workload": name, "gflop": fl / 1e9, "gpu_us": gpu_s * 1e6, "oracle_rows": o_rows,
+               "oracle_s": o_s, "oracle_extrapolated": o_ext, "blocked_rows": b_rows, "blocked_s": b_s,
+               "blocked_extrapolated": b_ext, "cores": threads, "cpu": model}
+        rows_out.append(rec)
+        mark = lambda e: " (extrapolated)" if e else ""
+        print(f"| {name} | {fl / 1e9:.3g} | {gpu_s * 1e6:.1f} | {o_rows} of {M} | {o_s:.3g}{mark(o_ext)} | "
+              f"{fl / o_s / 1e9:.1f} | {o_s / gpu_s:.3g}x | {b_rows} of {M} | {b_s:.3g}{mark(b_ext)} | "
+              f"{fl / b_s / 1e9:.1f} | {b_s / gpu_s:.3g}x |", flush=True)
+    print(json.dumps({"cpu_table": rows_out}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -257,6 +349,10 @@ def main():
     ap.add_argument("--table", action="store_true",
                     help="instead of the step: time every named workload (or --workload) through the "
                          "planner, warm and after a cache scrub, and print a markdown table")
+    ap.add_argument("--cpu-table", action="store_true",
+                    help="instead of the step: every named workload (or --workload) on the GPU and on the host "
+                         "(oracle and blocked CPU GEMM, whole problem or an extrapolated slab), as a markdown "
+                         "table")
     ap.add_argument("--split16-steps", type=int, default=10,
                     help="launches of the fp32 part through split fp16 inputs, reported beside the "
                          "step (0: skip)")
@@ -274,6 +370,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.table:
         workload_table(mg, torch, dev, tuple(args.workload) if args.workload else tuple(gi.WORKLOADS))
+        return
+    if args.cpu_table:
+        cpu_table(mg, torch, dev, tuple(args.workload) if args.workload else tuple(gi.WORKLOADS))
         return
     names = tuple(args.workload) if args.workload else STEP
 
@@ -339,20 +438,58 @@ def main():
         cold_ms = [sum(cev[k][i][0].elapsed_time(cev[k][i][1]) for k in range(args.cold_steps)) /
                    args.cold_steps for i in range(len(calls))]
         del scrub
-    clocks = None
-    if not args.no_clocks:
-        # clocks under the same load, read while an untimed copy of the step runs
-        import threading
-        box = {}
-        th = threading.Thread(target=lambda: box.setdefault("c", read_clocks()))
-        th.start()
-        t_end = time.perf_counter() + 30.0
-        while th.is_alive() and time.perf_counter() < t_end:
-            for _ in range(5):
-                step()
+    # Per part, outside the timed region: five trials of back-to-back
+    # launches (each trial at least ~100 ms of GPU time), per-launch median
+    # and minimum, with HIP events on the launch stream.
+    trials = []
+    for i, (name, w, Ad, Bd, Cd, ws) in enumerate(calls):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        launch(w, Ad, Bd, Cd, ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        reps = max(20, int(100.0 / max(e0.elapsed_time(e1), 1e-3)) + 1)
+        per = []
+        for _ in range(5):
+            e0.record(stream)
+            for _ in range(reps):
+                launch(w, Ad, Bd, Cd, ws)
+            e1.record(stream)
             torch.cuda.synchronize()
-        th.join()
-        clocks = box.get("c")
+            per.append(e0.elapsed_time(e1) / reps * 1e3)
+        trials.append({"trials": 5, "launches_per_trial": reps, "us_median": round(statistics.median(per), 2),
+                       "us_min": round(min(per), 2)})
+
+    clocks = None
+    part_clocks = [None] * len(calls)
+    if not args.no_clocks:
+        # Clocks under each part's own load: rocm-smi is read (a few times)
+        # while that part alone runs back to back, so each reading describes
+        # the kernel it is reported with.
+        import threading
+        for i, (name, w, Ad, Bd, Cd, ws) in enumerate(calls):
+            box = {"samples": []}
+
+            def sampler():
+                for _ in range(3):
+                    c = read_clocks()
+                    if c:
+                        box["samples"].append(c)
+
+            th = threading.Thread(target=sampler)
+            th.start()
+            t_end = time.perf_counter() + 30.0
+            while th.is_alive() and time.perf_counter() < t_end:
+                for _ in range(10):
+                    launch(w, Ad, Bd, Cd, ws)
+                torch.cuda.synchronize()
+            th.join()
+            sclk = [mhz for c in box["samples"] for k, v in c.items()
+                    if k.lower().startswith("sclk clock speed") and (mhz := _mhz(v)) is not None]
+            part_clocks[i] = {"sclk_mhz_samples": sclk,
+                              "sclk_mhz_median": statistics.median(sclk) if sclk else None,
+                              "readings": box["samples"][-1] if box["samples"] else None}
+        clocks = {calls[i][0]: part_clocks[i] for i in range(len(calls))}
 
     split16 = None
     f32_calls = [c for c in calls if c[1]["in_dtype"] == "f32"]
@@ -405,6 +542,9 @@ def main():
                       "min_hbm_bytes": min_bytes(w),
                       "split_k_workspace_bytes": 0 if calls[i][5] is None else calls[i][5].numel(),
                       "pages_context": PAGES_CONTEXT.get(name)})
+        parts[-1]["launch_trials"] = trials[i]
+        if part_clocks[i] is not None:
+            parts[-1]["sclk_mhz_under_own_load"] = part_clocks[i]["sclk_mhz_median"]
         if cold_ms is not None:
             parts[-1]["us_per_launch_cold"] = round(cold_ms[i] * 1e3, 2)
             parts[-1]["tflops_cold"] = round(flops(w) / (cold_ms[i] * 1e-3) / 1e12, 2)
@@ -424,7 +564,7 @@ def main():
         "dtype": "+".join(sorted({w["in_dtype"] for _, w, *_ in calls})),
         "data": "synthetic: seeded fp32 N(0,1) and fp16 N(0,1)/sqrt(K) matrices, resident in HBM",
         "config": {"workload": " + ".join(names), "parts": list(names)},
-        "parts": parts, "roofline": roofline, "gpu_clocks_under_load": clocks,
+        "parts": parts, "roofline": roofline, "gpu_clocks_per_part": clocks,
         "fp32_via_split_fp16": split16,
     }
     if not args.no_cpu and rank == 0:

@@ -80,9 +80,15 @@ def _target(args):
     Cd = C.to(dev) if C is not None else torch.zeros((w["M"], w["N"]), dtype=gi.DTYPES[w["c_dtype"]],
                                                      device=dev)
     cfg = -1 if args.config is None else mg.config_id(w["in_dtype"], args.config)
+    # the benchmark's launch configuration: gemm_ex with the planner's
+    # workspace when it asks for one (split-K, repacking, stream-K)
+    codes = mg.DTYPE_CODES
+    wsb = mg.workspace_size(codes[w["in_dtype"]], codes[w["c_dtype"]], int(w["ta"]), int(w["tb"]), w["M"], w["N"],
+                            w["K"], Ad.stride(0), Bd.stride(0)) if cfg < 0 else 0
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
     for _ in range(args.iters):
         mg.gemm(Ad, Bd, Cd, alpha=w["alpha"], beta=w["beta"], trans_a=w["ta"], trans_b=w["tb"],
-                config=cfg)
+                config=cfg, workspace=ws)
     torch.cuda.synchronize()
     print(f"{args.workload} x{args.iters} done", flush=True)
 
@@ -189,8 +195,16 @@ def run(args):
     import dense_gemm_12_amd as mg
     from dense_gemm_12_amd.srchash import kernel_src_hash
     lib = mg.load()
-    cfg_id = lib.mg_chosen_config(mg.DTYPE_CODES[w["in_dtype"]], mg.DTYPE_CODES[w["c_dtype"]],
-                                  int(w["ta"]), int(w["tb"]), w["M"], w["N"], w["K"])
+    codes = mg.DTYPE_CODES
+    lda = w["M"] if w["ta"] else w["K"]
+    ldb = w["K"] if w["tb"] else w["N"]
+    if mg.workspace_size(codes[w["in_dtype"]], codes[w["c_dtype"]], int(w["ta"]), int(w["tb"]), w["M"], w["N"],
+                         w["K"], lda, ldb):
+        cfg_id = mg.chosen_config_ws(w["in_dtype"], w["c_dtype"], int(w["ta"]), int(w["tb"]), w["M"], w["N"],
+                                     w["K"], lda, ldb)
+    else:
+        cfg_id = lib.mg_chosen_config(codes[w["in_dtype"]], codes[w["c_dtype"]], int(w["ta"]), int(w["tb"]),
+                                      w["M"], w["N"], w["K"])
     summary = {
         "workload": args.workload, "kernel": kname, "iters": args.iters,
         "config": args.config or mg.config_name(w["in_dtype"], cfg_id),
