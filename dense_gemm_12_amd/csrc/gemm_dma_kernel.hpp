@@ -108,6 +108,15 @@ __device__ __forceinline__ void lds_barrier() {
 //   is the sub-step-s value of 16-row block 4q + t, whose lane-j row is
 //   64q + 4j + t.  The tile therefore orders the rows of each 64-row quad as
 //   (4j + t), and the epilogue maps them back.
+// Whether DmaOperand<R, BK, KC, NW, ES> has a supported LDS layout: whole
+// 1 KiB DMA blocks per wave; k-contiguous rows of 64 or 128 bytes, or k-major
+// rows of at least 256 bytes that tile a 1 KiB block.
+template <int R, int BK, bool KC, int NW, int ES>
+constexpr bool dma_operand_ok() {
+  const int bytes = R * BK * ES, rowb = KC ? BK * ES : R * ES, cpr = rowb / 16;
+  return bytes % (1024 * NW) == 0 && (KC ? (cpr == 4 || cpr == 8) : (cpr >= 16 && 1024 % rowb == 0));
+}
+
 template <int R, int BK, bool KC, int NW, int ES = 2>
 struct DmaOperand {
   static constexpr int V = 16 / ES;

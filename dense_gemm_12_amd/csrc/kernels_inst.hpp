@@ -75,11 +75,21 @@ template <typename TI, typename TO, int BM, int BN, int BK, int ST, int WM, int 
 struct DmaLayoutSet {
   template <bool AKC, bool BKC>
   using T = DmaTile<TI, TO, BM, BN, BK, ST, WM, WN, AKC, BKC, PP, SK>;
+  // a layout whose operand slices have no supported LDS layout (e.g. a
+  // k-major operand of fewer than 128 16-bit rows) is left null
+  template <bool AKC, bool BKC>
+  static LaunchFn fn() {
+    constexpr int NW = WM * WN, ES = sizeof(TI);
+    if constexpr (dma_operand_ok<BM, BK, AKC, NW, ES>() && dma_operand_ok<BN, BK, BKC, NW, ES>())
+      return &launch_dma_tile<T<AKC, BKC>>;
+    else
+      return nullptr;
+  }
   static void fill(LaunchFn (&f)[2][2]) {
-    f[0][0] = &launch_dma_tile<T<false, false>>;
-    f[0][1] = &launch_dma_tile<T<false, true>>;
-    f[1][0] = &launch_dma_tile<T<true, false>>;
-    f[1][1] = &launch_dma_tile<T<true, true>>;
+    f[0][0] = fn<false, false>();
+    f[0][1] = fn<false, true>();
+    f[1][0] = fn<true, false>();
+    f[1][1] = fn<true, true>();
   }
 };
 

@@ -86,8 +86,14 @@ def test_every_config_every_layout_integer_bit_exact(in_dtype):
                     log("case " + what)
                     # stream-K configurations run only with a workspace (through gemm_ex)
                     ws = SK_WS_BYTES if name.endswith("_sk") else None
-                    got = run_gpu(A, B, C, alpha=1.5, beta=0.5, ta=ta, tb=tb, c_dtype=c_dtype,
-                                  config=cfg, workspace_bytes=ws)
+                    try:
+                        got = run_gpu(A, B, C, alpha=1.5, beta=0.5, ta=ta, tb=tb, c_dtype=c_dtype,
+                                      config=cfg, workspace_bytes=ws)
+                    except mg.MgemmError as e:
+                        # only the few-row tiles lack a layout: a k-major A of 64 rows
+                        assert e.status == mg.MG_EUNSUPPORTED and ta and "_64x" in name, (what, e)
+                        log(f"  {name}: no k-major A layout")
+                        continue
                     assert_bit_exact(got, ref, c_dtype, what)
 
 
@@ -112,8 +118,12 @@ def test_every_16bit_config_long_k_integer_bit_exact(in_dtype):
                 what = f"{name} ta={ta} tb={tb} c={c_dtype} {M}x{N}x{K}"
                 log("case " + what)
                 ws = SK_WS_BYTES if name.endswith("_sk") else None
-                got = run_gpu(A, B, C, alpha=1.0, beta=1.0, ta=ta, tb=tb, c_dtype=c_dtype, config=cfg,
-                              workspace_bytes=ws)
+                try:
+                    got = run_gpu(A, B, C, alpha=1.0, beta=1.0, ta=ta, tb=tb, c_dtype=c_dtype, config=cfg,
+                                  workspace_bytes=ws)
+                except mg.MgemmError as e:
+                    assert e.status == mg.MG_EUNSUPPORTED and ta and "_64x" in name, (what, e)
+                    continue
                 assert_bit_exact(got, ref, c_dtype, what)
 
 
