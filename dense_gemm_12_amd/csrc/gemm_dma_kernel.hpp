@@ -514,30 +514,34 @@ struct DmaTile {
           if (i + 1 < nk) end_phase();
         }
       }
-    } else if constexpr (STAGES == 2 && KSTEPS == 2) {
-      // Mid-slice barrier schedule.  Per slice kt (buffer S = kt % 2):
+    } else if constexpr (KSTEPS == 2) {
+      // Mid-slice barrier schedule.  Per slice kt (buffer S = kt % STAGES):
       //   phase A: MFMAs of k-step 0, each followed by at most one LDS read
       //            of the k-step 1 fragments of slice kt;
-      //   wait for slice kt+1's DMA and for this wave's reads; barrier: every
-      //   wave now holds all of slice kt's fragments, so buffer S is free;
+      //   wait for slice kt+1's DMA (slices kt+2 .. kt+STAGES-1 stay in
+      //   flight) and for this wave's reads; barrier: every wave now holds
+      //   all of slice kt's fragments, so buffer S is free;
       //   phase C: MFMAs of k-step 1, each followed by at most one DMA issue
-      //            for slice kt+2 (into S) or one LDS read of slice kt+1's
-      //            k-step 0 fragments.
+      //            for slice kt+STAGES (into S) or one LDS read of slice
+      //            kt+1's k-step 0 fragments.
       // (With more memory ops than MFMAs, each MFMA is followed by up to
       // ceil(ops / MFMAs) of them.)  The MFMAs never wait on an LDS read; the
-      // barrier is the only point where the matrix pipe can drain.
+      // barrier is the only point where the matrix pipe can drain.  With two
+      // stages a slice's DMA has one slice of time to land; every further
+      // stage adds one (the 4-wave 128 x 128 tiles, one workgroup per CU,
+      // need the second).
       constexpr int SLOTS = MFMAS;
       constexpr int PA = (RD_A + RD_B + SLOTS - 1) / SLOTS;                    // ops per MFMA, phase A
       constexpr int PC = (LOADS_PER_SLICE + RD_A + RD_B + SLOTS - 1) / SLOTS;  // ops per MFMA, phase C
       u32x4 fa0[MI], fb0[NJ], fa1[MI], fb1[NJ];
-      issue(0);
-      issue(1);
-      wait_vmcnt<LOADS_PER_SLICE>();  // slice 0 landed; slice 1 stays in flight
+#pragma unroll
+      for (int s = 0; s < STAGES; ++s) issue(s);
+      wait_vmcnt<LOADS_PER_SLICE * (STAGES - 1)>();  // slice 0 landed; the rest stay in flight
       lds_barrier();
       read_frags(lds, 0, fa0, fb0);
       for (int kt = 0; kt < nk; ++kt) {
-        const char *st = lds + (kt & 1) * STAGE_BYTES;
-        const char *nx = lds + ((kt + 1) & 1) * STAGE_BYTES;
+        const char *st = lds + (kt % STAGES) * STAGE_BYTES;
+        const char *nx = lds + ((kt + 1) % STAGES) * STAGE_BYTES;
         if constexpr (ASM_READS) wait_lgkm0_fenced();  // fa0 / fb0 (prologue or last phase C)
 #pragma unroll
         for (int t = 0; t < SLOTS; ++t) {  // phase A
@@ -547,15 +551,15 @@ struct DmaTile {
             if (o < RD_A + RD_B) read_op(st, 1, o, fa1, fb1);
           __builtin_amdgcn_sched_barrier(0);
         }
-        wait_vmcnt<0>();
+        wait_vmcnt<LOADS_PER_SLICE * (STAGES - 2)>();  // slice kt+1 landed
         wait_lgkm0_fenced();  // this wave's reads of S are done (phase C's fragments included)
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int t = 0; t < SLOTS; ++t) {  // phase C
           mfma(t, fa1, fb1);
 #pragma unroll
           for (int o = t * PC; o < (t + 1) * PC; ++o) {
-            if (o < LOADS_PER_SLICE) dma_op(kt + 2, o);
+            if (o < LOADS_PER_SLICE) dma_op(kt + STAGES, o);
             else if (o < LOADS_PER_SLICE + RD_A + RD_B) read_op(nx, 0, o - LOADS_PER_SLICE, fa0, fb0);
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -603,8 +607,8 @@ struct DmaTile {
         }
       }
     } else {
-      // Plain multistage loop: one barrier per slice, next k-step's
-      // fragments read while the current one's MFMAs run.
+      // Plain loop for one-k-step slices in two stages: one barrier per
+      // slice, the slice's fragments read right after it.
 #pragma unroll
       for (int s = 0; s < STAGES - 1; ++s) issue(s);
       for (int kt = 0; kt < nk; ++kt) {

@@ -13,6 +13,9 @@ const KernelEntry *entries_f16_vgpr(int *n) {
       make_dma_entry<_Float16, _Float16, 256, 128, 64, 2, 2, 2>("dma_f16_256x128x64_s2_w2x2"),
       make_dma_entry<_Float16, _Float16, 256, 128, 32, 4, 2, 2>("dma_f16_256x128x32_s4_w2x2"),
       make_dma_entry<_Float16, _Float16, 128, 128, 64, 3, 2, 2>("dma_f16_128x128x64_s3_w2x2"),
+      // eight waves (64 x 32 each, two per SIMD): one covers the other's barrier
+      make_dma_entry<_Float16, _Float16, 128, 128, 64, 3, 2, 4>("dma_f16_128x128x64_s3_w2x4"),
+      make_dma_entry<_Float16, _Float16, 128, 128, 64, 4, 2, 4>("dma_f16_128x128x64_s4_w2x4"),
       make_entry<_Float16, _Float16, 256, 128, 64, 2, 2, true, true>("mfma_f16_256x128x64_w2x2"),
       make_entry<_Float16, _Float16, 128, 256, 64, 2, 2, true, true>("mfma_f16_128x256x64_w2x2"),
       make_entry<_Float16, _Float16, 128, 128, 64, 2, 2, true, true>("mfma_f16_128x128x64_w2x2"),
