@@ -11,16 +11,19 @@ import pytest
 import torch
 
 import gemm_inputs as gi
-from gpu_helpers import assert_bit_exact, log, oracle_full
+from gpu_helpers import SK_WS_BYTES, assert_bit_exact, log, oracle_full
 
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # (label, workload or shape, through gemm_ex with a workspace)
-    ("fp16 TN 300x260x200 plain", ("f16", "f16", False, True, 300, 260, 200, 1.0, 0.0), False),
-    ("fp32 NN 256^3 split-K", "fp32_nn_256", True),
-    ("bf16 NN 127x4096x4095 repack + split-K", "bf16_nn_127x4096x4095", True),
-    ("fp32 NN 190x170x160 beta=0.5 plain", ("f32", "f32", False, False, 190, 170, 160, 1.5, 0.5), False),
+    # (label, workload or shape, through gemm_ex with a workspace, forced configuration)
+    ("fp16 TN 300x260x200 plain", ("f16", "f16", False, True, 300, 260, 200, 1.0, 0.0), False, None),
+    ("fp32 NN 256^3 split-K", "fp32_nn_256", True, None),
+    ("bf16 NN 127x4096x4095 repack + split-K", "bf16_nn_127x4096x4095", True, None),
+    ("fp32 NN 190x170x160 beta=0.5 plain", ("f32", "f32", False, False, 190, 170, 160, 1.5, 0.5), False, None),
+    # stream-K: a counter-zeroing kernel, then the persistent tile kernel with its last-arriver fixup
+    ("bf16 NN 1024x2816x1024 beta=0.5 stream-K", ("bf16", "f32", False, False, 1024, 2816, 1024, 1.0, 0.5), True,
+     "dma_bf16_256x256x64_s2_w2x4_sk"),
 ]
 
 
@@ -38,8 +41,8 @@ def _inputs(spec):
     return (ind, cd, ta, tb, alpha, beta, A, B, C)
 
 
-@pytest.mark.parametrize("label,spec,use_ws", CASES, ids=[c[0] for c in CASES])
-def test_captured_call_replays_match_eager(label, spec, use_ws):
+@pytest.mark.parametrize("label,spec,use_ws,cfg_name", CASES, ids=[c[0] for c in CASES])
+def test_captured_call_replays_match_eager(label, spec, use_ws, cfg_name):
     import dense_gemm_12_amd as mg
     dev = torch.device("cuda:0")
     ind, cd, ta, tb, alpha, beta, A, B, C = _inputs(spec)
@@ -50,15 +53,17 @@ def test_captured_call_replays_match_eager(label, spec, use_ws):
     C0 = (C if C is not None else torch.zeros((M, N), dtype=gi.DTYPES[cd])).to(dev)
     Cd = C0.clone()
     ws = None
+    cfg = -1 if cfg_name is None else mg.config_id(ind, cfg_name)
     if use_ws:
         codes = mg.DTYPE_CODES
-        nbytes = mg.workspace_size(codes[ind], codes[cd], int(ta), int(tb), M, N, K, Ad.stride(0), Bd.stride(0))
+        nbytes = (SK_WS_BYTES if cfg_name is not None else
+                  mg.workspace_size(codes[ind], codes[cd], int(ta), int(tb), M, N, K, Ad.stride(0), Bd.stride(0)))
         assert nbytes > 0
         ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     log(f"case {label}: eager")
 
     def call():
-        mg.gemm(Ad, Bd, Cd, alpha=alpha, beta=beta, trans_a=ta, trans_b=tb, workspace=ws)
+        mg.gemm(Ad, Bd, Cd, alpha=alpha, beta=beta, trans_a=ta, trans_b=tb, workspace=ws, config=cfg)
 
     call()
     torch.cuda.synchronize()
