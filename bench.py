@@ -17,8 +17,8 @@ stream) and the CPU oracle timed on a bounded sample of the same step.
 
 After the timed steps (outside the timed region): each part is timed again
 with cold caches (a 512 MiB write before every launch, events around the
-GEMM alone); the GPU clocks and power are read with rocm-smi while untimed
-steps run; and a cache-blocked CPU GEMM (cpu_gemm/, fp32 accumulation, all
+GEMM alone); the GPU clock (rocm-smi) and socket power (amd-smi) are read
+while each part alone runs untimed; and a cache-blocked CPU GEMM (cpu_gemm/, fp32 accumulation, all
 cores) runs the whole step as a second CPU baseline.  A workload whose tile
 grid leaves CUs idle runs through the split-K entry point with the
 workspace the planner asks for.  The fp32 part is also timed through
@@ -187,7 +187,25 @@ def read_clocks():
         key = k.lower()
         if key.startswith(("sclk", "mclk", "fclk", "socclk")) or "power" in key:
             out[k] = v
+    w = read_socket_power()
+    if w is not None:
+        out["socket_power_w"] = w
     return out or None
+
+
+def read_socket_power():
+    """Socket power in W from amd-smi (rocm-smi reports none on this
+    device); None where it cannot say.  The value is refreshed about once a
+    second."""
+    try:
+        r = subprocess.run(["amd-smi", "metric", "--power", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        data = json.loads(r.stdout)
+        gpus = data["gpu_data"] if isinstance(data, dict) else data
+        v = gpus[0]["power"]["socket_power"]
+        return float(v["value"] if isinstance(v, dict) else v)
+    except Exception:
+        return None
 
 
 def workload_table(mg, torch, dev, names):
@@ -345,7 +363,7 @@ def main():
                     help=f"named workloads instead of the metric's step {STEP}")
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="extra steps with a 512 MiB cache scrub before each launch (0: skip)")
-    ap.add_argument("--no-clocks", action="store_true", help="skip the rocm-smi clock reading")
+    ap.add_argument("--no-clocks", action="store_true", help="skip the clock and power readings")
     ap.add_argument("--table", action="store_true",
                     help="instead of the step: time every named workload (or --workload) through the "
                          "planner, warm and after a cache scrub, and print a markdown table")
@@ -463,18 +481,23 @@ def main():
     clocks = None
     part_clocks = [None] * len(calls)
     if not args.no_clocks:
-        # Clocks under each part's own load: rocm-smi is read (a few times)
-        # while that part alone runs back to back, so each reading describes
+        # Clocks and socket power under each part's own load: rocm-smi and
+        # amd-smi are read for about 3 s while that part alone runs back to
+        # back, and only readings from the last 1.5 s are kept (the power
+        # figure is refreshed about once a second), so each reading describes
         # the kernel it is reported with.
         import threading
         for i, (name, w, Ad, Bd, Cd, ws) in enumerate(calls):
             box = {"samples": []}
+            t_start = time.perf_counter()
 
             def sampler():
-                for _ in range(3):
+                while time.perf_counter() - t_start < 3.0:
                     c = read_clocks()
-                    if c:
+                    if c and time.perf_counter() - t_start >= 1.5:
                         box["samples"].append(c)
+                    elif not c:
+                        time.sleep(0.2)
 
             th = threading.Thread(target=sampler)
             th.start()
@@ -486,8 +509,10 @@ def main():
             th.join()
             sclk = [mhz for c in box["samples"] for k, v in c.items()
                     if k.lower().startswith("sclk clock speed") and (mhz := _mhz(v)) is not None]
+            pw = [c["socket_power_w"] for c in box["samples"] if c.get("socket_power_w") is not None]
             part_clocks[i] = {"sclk_mhz_samples": sclk,
                               "sclk_mhz_median": statistics.median(sclk) if sclk else None,
+                              "socket_power_w_median": statistics.median(pw) if pw else None,
                               "readings": box["samples"][-1] if box["samples"] else None}
         clocks = {calls[i][0]: part_clocks[i] for i in range(len(calls))}
 
@@ -545,6 +570,7 @@ def main():
         parts[-1]["launch_trials"] = trials[i]
         if part_clocks[i] is not None:
             parts[-1]["sclk_mhz_under_own_load"] = part_clocks[i]["sclk_mhz_median"]
+            parts[-1]["socket_power_w_under_own_load"] = part_clocks[i]["socket_power_w_median"]
         if cold_ms is not None:
             parts[-1]["us_per_launch_cold"] = round(cold_ms[i] * 1e3, 2)
             parts[-1]["tflops_cold"] = round(flops(w) / (cold_ms[i] * 1e-3) / 1e12, 2)

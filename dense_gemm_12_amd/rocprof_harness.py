@@ -86,7 +86,10 @@ def _target(args):
     wsb = mg.workspace_size(codes[w["in_dtype"]], codes[w["c_dtype"]], int(w["ta"]), int(w["tb"]), w["M"], w["N"],
                             w["K"], Ad.stride(0), Bd.stride(0)) if cfg < 0 else 0
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
-    for _ in range(args.iters):
+    # warm-up launches first (not profiled: the counter passes select the
+    # measured dispatches by iteration), so the measured ones run at the
+    # clock and power state of sustained load
+    for _ in range(args.warmup + args.iters):
         mg.gemm(Ad, Bd, Cd, alpha=w["alpha"], beta=w["beta"], trans_a=w["ta"], trans_b=w["tb"],
                 config=cfg, workspace=ws)
     torch.cuda.synchronize()
@@ -113,15 +116,30 @@ def _read_counters(pass_dir):
     return per
 
 
+def _last(per_kernel, n):
+    """The kernel's last n dispatches (by dispatch id): the measured ones
+    even if the profiler also counted warm-up dispatches."""
+    if per_kernel is None:
+        return None
+    keys = sorted(per_kernel["dispatch"], key=lambda k: float(k) if k not in (None, "") else -1.0)
+    return {"dispatch": {k: per_kernel["dispatch"][k] for k in keys[-n:]}}
+
+
 def _avg(per_kernel, counter):
     vals = [d[counter] for d in per_kernel["dispatch"].values() if counter in d]
     return sum(vals) / len(vals) if vals else None
 
 
-def _run_pass(name, counters, target_args, out):
+def _run_pass(name, counters, target_args, out, iterations=None):
+    """One --pmc pass; iterations = (first, last): only those dispatches of
+    the GEMM kernel (1-based, in launch order) get counters."""
     pdir = os.path.join(out, name)
     os.makedirs(pdir, exist_ok=True)
-    cmd = ["rocprofv3", "--pmc", *counters, "--output-format", "csv", "-d", pdir, "-o", name, "--",
+    sel = []
+    if iterations is not None:
+        sel = ["--kernel-include-regex", "gemm", "--kernel-iteration-range",
+               f"[{iterations[0]}-{iterations[1]}]"]
+    cmd = ["rocprofv3", "--pmc", *counters, *sel, "--output-format", "csv", "-d", pdir, "-o", name, "--",
            sys.executable, "-m", "dense_gemm_12_amd.rocprof_harness", "target", *target_args]
     print("pass:", " ".join(cmd), flush=True)
     t0 = time.time()
@@ -130,6 +148,30 @@ def _run_pass(name, counters, target_args, out):
     print(f"pass {name}: rc={r.returncode} in {time.time() - t0:.1f}s", flush=True)
     # rocprofv3 may exit non-zero after a complete run; the CSV decides.
     return _read_counters(pdir)
+
+
+def _run_trace(name, target_args, out):
+    """Kernel durations (ns) from a kernel-trace run with no counters:
+    {kernel name: [duration per dispatch, in launch order]}."""
+    pdir = os.path.join(out, name)
+    os.makedirs(pdir, exist_ok=True)
+    cmd = ["rocprofv3", "--kernel-trace", "--output-format", "csv", "-d", pdir, "-o", name, "--",
+           sys.executable, "-m", "dense_gemm_12_amd.rocprof_harness", "target", *target_args]
+    print("pass:", " ".join(cmd), flush=True)
+    t0 = time.time()
+    r = subprocess.run(cmd, cwd="/tmp", env={**os.environ, "TMPDIR": "/tmp", "PYTHONPATH": ROOT},
+                       timeout=300)
+    print(f"pass {name}: rc={r.returncode} in {time.time() - t0:.1f}s", flush=True)
+    files = glob.glob(os.path.join(pdir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise RuntimeError(f"no kernel_trace.csv under {pdir}")
+    per = {}
+    for f in files:
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                per.setdefault(row["Kernel_Name"], []).append(
+                    (float(row["Start_Timestamp"]), float(row["End_Timestamp"]) - float(row["Start_Timestamp"])))
+    return {k: [d for _, d in sorted(v)] for k, v in per.items()}  # durations in launch order
 
 
 def _pick(per, want):
@@ -146,12 +188,19 @@ def run(args):
     import gemm_inputs as gi
     out = os.path.abspath(args.out)
     os.makedirs(out, exist_ok=True)
-    tgt = ["--workload", args.workload, "--iters", str(args.iters)]
+    w = gi.WORKLOADS[args.workload]
+    # about 1.5 s of warm-up launches (estimated at half the peak rate),
+    # 20 to 30000 of them
+    est_s = 2.0 * w["M"] * w["N"] * w["K"] / (0.5 * PEAK_TFLOPS[w["in_dtype"]] * 1e12)
+    warm = int(min(30000, max(20, 1.5 / est_s))) if args.warmup < 0 else args.warmup
+    tgt = ["--workload", args.workload, "--iters", str(args.iters), "--warmup", str(warm)]
     if args.config:
         tgt += ["--config", args.config]
+    measured = (warm + 1, warm + args.iters)
     results = {}
     for name, counters in PASSES.items():
-        results[name] = _run_pass(name, counters, tgt, out)
+        results[name] = _run_pass(name, counters, tgt, out, iterations=measured)
+    trace = _run_trace("trace", tgt, out)
     calib = {}
     for name in ("fetch", "write", "dram"):
         calib[name] = _run_pass("copy_" + name, PASSES[name], ["--workload", "copy", "--iters", "3"],
@@ -168,7 +217,7 @@ def run(args):
 
     w = gi.WORKLOADS[args.workload]
     flops = 2.0 * w["M"] * w["N"] * w["K"]
-    sq = results["sq"][kname]
+    sq = _last(results["sq"][kname], args.iters)
     gui = _avg(sq, "GRBM_GUI_ACTIVE")
     mfma = _avg(sq, "SQ_VALU_MFMA_BUSY_CYCLES")
     valu = _avg(sq, "SQ_ACTIVE_INST_VALU")
@@ -177,14 +226,17 @@ def run(args):
     durs = [d["End_Timestamp"] - d["Start_Timestamp"] for d in sq["dispatch"].values()
             if "End_Timestamp" in d]
     dur_ns = sorted(durs)[len(durs) // 2] if durs else None
+    tk = _pick({k: {"dispatch": dict(enumerate(v))} for k, v in trace.items()}, "gemm")
+    tr = sorted(trace[tk][-args.iters:]) if tk else []  # the measured launches, after the warm-up
+    trace_ns = tr[len(tr) // 2] if tr else None
     # GRBM_GUI_ACTIVE is reported per XCD and summed over the 8 XCDs.
     gui_cycles = gui / 8 if gui else None
-    fetch_kib = _avg(results["fetch"][_pick(results["fetch"], "gemm")], "FETCH_SIZE")
-    write_kib = _avg(results["write"][_pick(results["write"], "gemm")], "WRITE_SIZE")
-    dr = results["dram"][_pick(results["dram"], "gemm")]
+    fetch_kib = _avg(_last(results["fetch"][_pick(results["fetch"], "gemm")], args.iters), "FETCH_SIZE")
+    write_kib = _avg(_last(results["write"][_pick(results["write"], "gemm")], args.iters), "WRITE_SIZE")
+    dr = _last(results["dram"][_pick(results["dram"], "gemm")], args.iters)
     dram_rd = _avg(dr, "TCC_EA0_RDREQ_DRAM_32B_sum")
     dram_wr = _avg(dr, "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum")
-    der = results["derived"][_pick(results["derived"], "gemm")]
+    der = _last(results["derived"][_pick(results["derived"], "gemm")], args.iters)
     sdk_mfma = _avg(der, "MfmaUtil")
     sdk_valu = _avg(der, "VALUBusy")
     es = 4 if w["in_dtype"] == "f32" else 2
@@ -209,10 +261,14 @@ def run(args):
         "workload": args.workload, "kernel": kname, "iters": args.iters,
         "config": args.config or mg.config_name(w["in_dtype"], cfg_id),
         "src_hash": kernel_src_hash(),
+        "warmup_launches": warm,
         "dispatches": len(sq["dispatch"]),
+        "kernel_ns_median": trace_ns,
         "kernel_ns_median_under_pmc": dur_ns,
         "gui_active_cycles": gui_cycles,
-        "effective_clock_ghz": (gui_cycles / dur_ns) if (gui_cycles and dur_ns) else None,
+        # cycles counted in the counter pass over the measured launches'
+        # duration in the kernel-trace pass
+        "effective_clock_ghz": (gui_cycles / trace_ns) if (gui_cycles and trace_ns) else None,
         "mfma_util_pct": 100.0 * mfma / (gui_cycles * SIMDS) if (mfma and gui_cycles) else None,
         "valu_busy_pct": 100.0 * valu / CUS / gui_cycles if (valu and gui_cycles) else None,
         "lds_bank_conflict_per_access": bank / (ldsact - bank) if (ldsact and ldsact > bank) else None,
@@ -232,13 +288,13 @@ def run(args):
         "min_bytes_per_launch": min_bytes,
         "flops_per_launch": flops,
     }
-    if dur_ns:
-        summary["tflops_under_pmc"] = flops / dur_ns / 1e3
-        summary["frac_of_peak_under_pmc"] = summary["tflops_under_pmc"] / PEAK_TFLOPS[w["in_dtype"]]
+    if trace_ns:
+        summary["tflops"] = flops / trace_ns / 1e3
+        summary["frac_of_peak"] = summary["tflops"] / PEAK_TFLOPS[w["in_dtype"]]
         if summary["l2_miss_bytes_per_launch"]:
-            summary["l2_miss_gbps"] = summary["l2_miss_bytes_per_launch"] / dur_ns
+            summary["l2_miss_gbps"] = summary["l2_miss_bytes_per_launch"] / trace_ns
         if dram_rd is not None and dram_wr is not None:
-            summary["dram_gbps"] = (dram_rd + dram_wr) * 32 / dur_ns
+            summary["dram_gbps"] = (dram_rd + dram_wr) * 32 / trace_ns
             summary["dram_frac_of_hbm_peak"] = summary["dram_gbps"] / HBM_GBPS
     # The raw-counter derivations must agree with rocprofiler-sdk's own
     # (different passes, so a few per cent of run-to-run spread is allowed).
@@ -285,8 +341,12 @@ def collect(dirs, profiles):
                f"{s.get('iters', 5)} --out $OUT/harness_{w}")
         text = (f"# Hardware counters: {w}\n\n"
                 "Command ($OUT: any scratch directory; each counter group is one rocprofv3 --pmc pass over "
-                "the workload, plus three passes over a 1 GiB copy for calibrating FETCH_SIZE, WRITE_SIZE "
-                "and the DRAM request counters):\n\n"
+                "the workload, then one --kernel-trace pass without counters for the kernel's duration; "
+                "each run first launches the GEMM unprofiled for about 1.5 s (warmup_launches) and counts "
+                "only the measured launches after it (--kernel-iteration-range), so the figures describe "
+                "sustained load, "
+                "plus three passes over a 1 GiB copy for calibrating FETCH_SIZE, WRITE_SIZE and the DRAM "
+                "request counters):\n\n"
                 f"```\n{cmd}\n```\n\nKernel configuration `{s['config']}`, kernel source hash "
                 f"`{s['src_hash']}`.\n{body}\n"
                 f"Calibration: a {cal['bytes_each_way']} B device copy reads FETCH_SIZE = "
@@ -299,8 +359,13 @@ def collect(dirs, profiles):
                 "hits (the copy calibration shows how they relate to bytes moved).\n"
                 "valu_busy_pct / mfma_util_pct are derived from the raw counters with rocprofiler-sdk's "
                 "formulas; sdk_* are the SDK's own derived counters from a separate pass.\n"
+                "Times, rates and the effective clock (GRBM_GUI_ACTIVE cycles per ns) use the measured "
+                "launches' durations from the kernel-trace pass without counters "
+                "(kernel_ns_median_under_pmc is the same launches' duration in the counter pass). "
                 "GRBM_GUI_ACTIVE covers a little time around each dispatch, so for short kernels "
-                "(about 100 us) the effective clock reads high and the MFMA utilisation low.\n")
+                "(tens of us) the effective clock reads high and the MFMA utilisation low, and the raw and "
+                "SDK figures, taken in different passes, can differ by more than the 10 % the "
+                "*_agrees_with_sdk flags allow.\n")
         with open(os.path.join(profiles, f"counters_{w}.md"), "w") as f:
             f.write(text)
         print(f"{w}: {s['config']} {s['l2_miss_bytes_per_launch']:.4g} L2-miss B/launch")
@@ -316,11 +381,14 @@ def main():
     t.add_argument("--workload", required=True)
     t.add_argument("--iters", type=int, default=10)
     t.add_argument("--config", default=None)
+    t.add_argument("--warmup", type=int, default=0)
     r = sub.add_parser("run")
     r.add_argument("--workload", required=True)
     r.add_argument("--iters", type=int, default=10)
     r.add_argument("--config", default=None)
     r.add_argument("--out", required=True)
+    r.add_argument("--warmup", type=int, default=-1,
+                   help="unprofiled launches before the measured ones (default: about 1.5 s of them)")
     c = sub.add_parser("collect")
     c.add_argument("dirs", nargs="+")
     c.add_argument("--profiles", default=os.path.join(ROOT, "profiles"))
