@@ -162,6 +162,12 @@ def _run_trace(name, target_args, out):
     r = subprocess.run(cmd, cwd="/tmp", env={**os.environ, "TMPDIR": "/tmp", "PYTHONPATH": ROOT},
                        timeout=300)
     print(f"pass {name}: rc={r.returncode} in {time.time() - t0:.1f}s", flush=True)
+    return _read_trace(pdir)
+
+
+def _read_trace(pdir):
+    """{kernel name: [duration (ns) per dispatch, in launch order]} from the
+    kernel_trace.csv files under pdir."""
     files = glob.glob(os.path.join(pdir, "**", "*kernel_trace.csv"), recursive=True)
     if not files:
         raise RuntimeError(f"no kernel_trace.csv under {pdir}")

@@ -58,3 +58,26 @@ def test_kernel_hash_follows_device_sources_only(tmp_path):
     with open(pkg / "build.py", "a") as f:
         f.write("\n# flags\n")
     assert srchash.kernel_src_hash(str(pkg)) != h1
+
+
+def test_harness_keeps_the_measured_dispatches_and_trace_order(tmp_path):
+    """The counter harness counts only the launches after its warm-up: it
+    keeps a kernel's last n dispatches by numeric dispatch id (also if the
+    profiler counted more), and reads kernel-trace durations in launch order."""
+    from dense_gemm_12_amd import rocprof_harness as rh
+    per = {"dispatch": {str(i): {"X": float(i)} for i in (3, 10, 1, 2, 11, 9)}}
+    last = rh._last(per, 3)
+    assert sorted(last["dispatch"]) == ["10", "11", "9"]
+    assert rh._avg(last, "X") == 10.0
+    assert rh._last(None, 3) is None
+    d = tmp_path / "trace" / "host"
+    d.mkdir(parents=True)
+    rows = [("mg::gemm_dma_kernel", 300, 350), ("mg::gemm_dma_kernel", 100, 120), ("copy", 50, 60),
+            ("mg::gemm_dma_kernel", 200, 230)]
+    with open(d / "t_kernel_trace.csv", "w") as f:
+        f.write("Kernel_Name,Start_Timestamp,End_Timestamp\n")
+        for k, a, b in rows:
+            f.write(f"{k},{a},{b}\n")
+    tr = rh._read_trace(str(tmp_path / "trace"))
+    assert tr["mg::gemm_dma_kernel"] == [20.0, 30.0, 50.0]
+    assert tr["copy"] == [10.0]
