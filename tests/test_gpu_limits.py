@@ -3,7 +3,6 @@ tile's 256 rows span up to 255 x 2^23 bytes < 2^31 in the kernels' 32-bit
 buffer offsets), on every input type and both storage orders of A, against
 the oracle (bit-exact on integer data).  The operands live in wide device
 buffers whose padding holds NaN, which a correct kernel never reads."""
-import numpy as np
 import pytest
 import torch
 

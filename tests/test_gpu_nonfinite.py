@@ -9,7 +9,6 @@ give exactly the oracle's classes, and bit-exact values where finite.  NaN
 payloads are not compared."""
 import numpy as np
 import pytest
-import torch
 
 import gemm_inputs as gi
 from gpu_helpers import SK_WS_BYTES, log, oracle_full, out_as_f64, run_gpu, stored_shapes
