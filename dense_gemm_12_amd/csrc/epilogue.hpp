@@ -34,7 +34,7 @@ __device__ __forceinline__ GemmParams partial_params(const GemmParams &p, int kb
 //   cols, CQ = false: n = nw + 16j + 4(l/16) + v, four consecutive columns;
 //   cols, CQ = true:  n = nw + 64(j/4) + 16(l/16) + 4v + j%4, so the four
 //                     blocks of a quad give each lane 16 consecutive columns.
-template <typename TO, int MI, int NJ, bool RQ = false, bool CQ = false>
+template <typename TO, int MI, int NJ, bool RQ = false, bool CQ = false, bool WIDE = true>
 struct GemmEpilogue {
   static_assert(!RQ || MI % 4 == 0, "row quads need whole quads");
   static_assert(!CQ || NJ % 4 == 0, "column quads need whole quads");
@@ -94,6 +94,90 @@ struct GemmEpilogue {
     for (int e = 0; e < 4; ++e) x[e] = ldexpf(x[e], -(re + p.col_exp[min(n + e, p.N - 1)]));
   }
 
+  // Column quads store badly as they are: component v of block 4q + c is
+  // column 16g + 4v + c of the quad (g = lane / 16), so one store instruction
+  // would cover each row in four 16-byte pieces 64 bytes apart (measured: the
+  // fp32 NN 256 x 256 tiles lost ~6 % to it).  A 4 x 4 transpose of (lane
+  // group, component) with the lane-row swaps of gfx950 (v_permlane32_swap:
+  // lane groups 2, 3 of the first operand <-> 0, 1 of the second;
+  // v_permlane16_swap: groups 1, 3 of the first <-> 0, 2 of the second; each
+  // lane keeps its position within its group) turns component v of lane
+  // group g into column 16v + 4g + c, so that every store covers 64
+  // contiguous bytes of a row.  A group and its partners hold the same rows,
+  // so they are active together.
+  static __device__ __forceinline__ void transpose_quad(f32x4 &b) {
+    // (element values first: a bit cast of an ext-vector element lvalue reads element 0)
+    const float f0 = b[0], f1 = b[1], f2 = b[2], f3 = b[3];
+    uint32_t r0 = __builtin_bit_cast(uint32_t, f0), r1 = __builtin_bit_cast(uint32_t, f1);
+    uint32_t r2 = __builtin_bit_cast(uint32_t, f2), r3 = __builtin_bit_cast(uint32_t, f3);
+    auto s02 = __builtin_amdgcn_permlane32_swap(r0, r2, false, false);
+    auto s13 = __builtin_amdgcn_permlane32_swap(r1, r3, false, false);
+    auto s01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+    auto s23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+    b = f32x4{__builtin_bit_cast(float, (uint32_t)s01[0]), __builtin_bit_cast(float, (uint32_t)s01[1]),
+              __builtin_bit_cast(float, (uint32_t)s23[0]), __builtin_bit_cast(float, (uint32_t)s23[1])};
+  }
+
+  // 16-bit C: lane group g holds columns 4g .. 4g + 3 of each 16-column
+  // block, so a store covers 32 bytes of a row.  For a pair of blocks
+  // (a = block 2jj, b = block 2jj + 1), v_permlane32_swap(a, b) then
+  // v_permlane16_swap on the results leave lane group g with columns
+  // 8g .. 8g + 7 of the 32-column pair (first four in a, last four in b),
+  // so each lane stores 16 bytes and a store covers 64 contiguous bytes of a
+  // row (measured: fp16 TN 4096^3 3 % faster).
+  static __device__ __forceinline__ void transpose_pair(f32x4 &a, f32x4 &b) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float fa = a[c], fb = b[c];  // element values first (see transpose_quad)
+      auto s = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, fa), __builtin_bit_cast(uint32_t, fb),
+                                                false, false);
+      auto t = __builtin_amdgcn_permlane16_swap(s[0], s[1], false, false);
+      a[c] = __builtin_bit_cast(float, (uint32_t)t[0]);
+      b[c] = __builtin_bit_cast(float, (uint32_t)t[1]);
+    }
+  }
+
+  // C[m][n .. n+7] = alpha * x + beta * C for 16-bit C: one 16-byte access
+  // where the row allows it (c_vec >= 2), else two four-column stores.
+  static __device__ __forceinline__ void store8(const GemmParams &p, TO *crow, int n, const float (&x)[8],
+                                                bool use_beta) {
+    static_assert(sizeof(TO) == 2, "16-bit output");
+    if (p.c_vec >= 2 && n + 7 < p.N) {
+      const float alpha = p.alpha, beta = p.beta;
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = alpha * x[e];
+      u32x4 *cp = reinterpret_cast<u32x4 *>(crow + n);
+      if (use_beta) {
+        const u32x4 c = *cp;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint16_t bits = (uint16_t)(c[e >> 1] >> (16 * (e & 1)));
+          v[e] = fmaf(beta, to_f32(__builtin_bit_cast(TO, bits)), v[e]);
+        }
+      }
+      u32x4 o;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t lo = __builtin_bit_cast(uint16_t, from_f32<TO>(v[2 * d]));
+        const uint32_t hi = __builtin_bit_cast(uint16_t, from_f32<TO>(v[2 * d + 1]));
+        o[d] = lo | (hi << 16);
+      }
+      *cp = o;
+    } else {
+      const float x0[4] = {x[0], x[1], x[2], x[3]}, x1[4] = {x[4], x[5], x[6], x[7]};
+      store4(p, crow, n, x0, use_beta);
+      store4(p, crow, n + 4, x1, use_beta);
+    }
+  }
+
+  // Four-column stores are kept where registers are short: with WIDE =
+  // false (the stream-K tiles: the pair transpose's registers, live across
+  // their loop over work units, pushed the register allocator into reusing
+  // an in-flight LDS read's destination) and for more than 32 accumulator
+  // blocks per lane (the four-wave 256 x 256 tiles, which then spilled).
+  static constexpr bool PAIRS = WIDE && !CQ && sizeof(TO) == 2 && NJ % 2 == 0 && MI * NJ <= 32;
+
   static __device__ __forceinline__ void store(const GemmParams &p, const f32x4 (&acc)[MI][NJ],
                                                int mw, int nw, int lane) {
     TO *C = static_cast<TO *>(p.C);
@@ -102,15 +186,44 @@ struct GemmEpilogue {
     const int r = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
+      f32x4 blk[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        blk[j] = acc[i][j];
+        if constexpr (CQ) transpose_quad(blk[j]);  // before any lane leaves the loop
+      }
+      if constexpr (PAIRS) {
+#pragma unroll
+        for (int jj = 0; jj < NJ / 2; ++jj) transpose_pair(blk[2 * jj], blk[2 * jj + 1]);
+      }
       const int m = RQ ? mw + 64 * (i >> 2) + 4 * r + (i & 3) : mw + i * 16 + r;
       if (m >= p.M) continue;
       TO *crow = C + (int64_t)m * p.ldc;
-      if constexpr (!CQ) {
+      if constexpr (PAIRS) {
+#pragma unroll
+        for (int jj = 0; jj < NJ / 2; ++jj) {
+          const int n = nw + jj * 32 + g * 8;  // after transpose_pair
+          if (n >= p.N) continue;
+          float x[8] = {blk[2 * jj][0],     blk[2 * jj][1],     blk[2 * jj][2],     blk[2 * jj][3],
+                        blk[2 * jj + 1][0], blk[2 * jj + 1][1], blk[2 * jj + 1][2], blk[2 * jj + 1][3]};
+          if (scaled) {
+            float x0[4] = {x[0], x[1], x[2], x[3]}, x1[4] = {x[4], x[5], x[6], x[7]};
+            unscale(p, m, n, x0);
+            unscale(p, m, n + 4, x1);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              x[e] = x0[e];
+              x[4 + e] = x1[e];
+            }
+          }
+          store8(p, crow, n, x, use_beta);
+        }
+      } else if constexpr (!CQ) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
           const int n = nw + j * 16 + g * 4;
           if (n >= p.N) continue;
-          float x[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+          float x[4] = {blk[j][0], blk[j][1], blk[j][2], blk[j][3]};
           if (scaled) unscale(p, m, n, x);
           store4(p, crow, n, x, use_beta);
         }
@@ -119,10 +232,9 @@ struct GemmEpilogue {
         for (int q = 0; q < NJ / 4; ++q)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const int n = nw + 64 * q + 16 * g + 4 * v;
+            const int n = nw + 64 * q + 16 * v + 4 * g;  // after transpose_quad
             if (n >= p.N) continue;
-            float x[4] = {acc[i][4 * q][v], acc[i][4 * q + 1][v], acc[i][4 * q + 2][v],
-                          acc[i][4 * q + 3][v]};
+            float x[4] = {blk[4 * q][v], blk[4 * q + 1][v], blk[4 * q + 2][v], blk[4 * q + 3][v]};
             if (scaled) unscale(p, m, n, x);
             store4(p, crow, n, x, use_beta);
           }

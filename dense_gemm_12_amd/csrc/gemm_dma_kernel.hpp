@@ -385,7 +385,7 @@ struct DmaTile {
                   f32x4, __builtin_amdgcn_raw_buffer_load_b128(ws, sq + (i * NJ + j) * 1024, 0, kDeviceScope));
         }
       }
-      GemmEpilogue<TO, MI, NJ, A_Q, B_Q>::store(p, acc, m0 + wm * WTM, n0 + wn * WTN, ln);
+      GemmEpilogue<TO, MI, NJ, A_Q, B_Q, false>::store(p, acc, m0 + wm * WTM, n0 + wn * WTN, ln);
     }
   }
 

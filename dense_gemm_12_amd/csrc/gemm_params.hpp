@@ -15,7 +15,7 @@ struct GemmParams {
   float alpha, beta;
   int tiles_m, tiles_n;   // grid = tiles_m * tiles_n workgroups
   int group_m;            // tile-rows per raster group
-  int c_vec;              // C rows allow 16-byte (fp32) / 8-byte (16-bit) access
+  int c_vec;              // C rows allow 16-byte (fp32) / 8-byte (16-bit) access; 2: 16-byte 16-bit too
   // Split-K.  splits == 1: one workgroup per tile covers all of K and the
   // epilogue writes C.  splits > 1: the grid is tiles * splits, split s
   // covers k in [s * k_chunk, min(K, (s + 1) * k_chunk)) and writes its fp32

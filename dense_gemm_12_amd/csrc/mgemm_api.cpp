@@ -422,7 +422,10 @@ static mg_status run(const Problem &p, int forced, int splits, void *ws, size_t 
   gp.row_exp = row_exp;
   gp.col_exp = col_exp;
   const int ces = elem_size(p.c_type);
+  // 1: four-element (16-byte fp32, 8-byte 16-bit) C accesses are legal;
+  // 2: eight-element (16-byte) 16-bit C accesses too
   gp.c_vec = ((uintptr_t)p.C % (ces == 4 ? 16 : 8) == 0) && (p.ldc % 4 == 0);
+  if (gp.c_vec && ces == 2 && (uintptr_t)p.C % 16 == 0 && p.ldc % 8 == 0) gp.c_vec = 2;
   const int c_idx = p.c_type == MG_F32 ? 0 : (p.c_type == MG_F16 ? 1 : 2);
 
   hipError_t err;
