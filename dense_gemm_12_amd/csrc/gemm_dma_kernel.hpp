@@ -532,7 +532,11 @@ struct DmaTile {
       // need the second).
       constexpr int SLOTS = MFMAS;
       constexpr int PA = (RD_A + RD_B + SLOTS - 1) / SLOTS;                    // ops per MFMA, phase A
-      constexpr int PC = (LOADS_PER_SLICE + RD_A + RD_B + SLOTS - 1) / SLOTS;  // ops per MFMA, phase C
+      // phase C: the next k-step's reads first (PCR after each MFMA), and the
+      // slice's DMA spread evenly, one after every DSTR-th MFMA
+      constexpr int PCR = (RD_A + RD_B + SLOTS - 1) / SLOTS;
+      static_assert(LOADS_PER_SLICE <= SLOTS, "one DMA issue per MFMA at most");
+      constexpr int DSTR = SLOTS / LOADS_PER_SLICE;
       u32x4 fa0[MI], fb0[NJ], fa1[MI], fb1[NJ];
 #pragma unroll
       for (int s = 0; s < STAGES; ++s) issue(s);
@@ -558,10 +562,9 @@ struct DmaTile {
         for (int t = 0; t < SLOTS; ++t) {  // phase C
           mfma(t, fa1, fb1);
 #pragma unroll
-          for (int o = t * PC; o < (t + 1) * PC; ++o) {
-            if (o < LOADS_PER_SLICE) dma_op(kt + STAGES, o);
-            else if (o < LOADS_PER_SLICE + RD_A + RD_B) read_op(nx, 0, o - LOADS_PER_SLICE, fa0, fb0);
-          }
+          for (int o = t * PCR; o < (t + 1) * PCR; ++o)
+            if (o < RD_A + RD_B) read_op(nx, 0, o, fa0, fb0);
+          if (t % DSTR == 0 && t / DSTR < LOADS_PER_SLICE) dma_op(kt + STAGES, t / DSTR);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
