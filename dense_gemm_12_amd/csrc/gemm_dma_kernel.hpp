@@ -521,11 +521,13 @@ struct DmaTile {
       //   wait for slice kt+1's DMA (slices kt+2 .. kt+STAGES-1 stay in
       //   flight) and for this wave's reads; barrier: every wave now holds
       //   all of slice kt's fragments, so buffer S is free;
-      //   phase C: MFMAs of k-step 1, each followed by at most one DMA issue
-      //            for slice kt+STAGES (into S) or one LDS read of slice
-      //            kt+1's k-step 0 fragments.
-      // (With more memory ops than MFMAs, each MFMA is followed by up to
-      // ceil(ops / MFMAs) of them.)  The MFMAs never wait on an LDS read; the
+      //   phase C: MFMAs of k-step 1, each followed by LDS reads of slice
+      //            kt+1's k-step 0 fragments, and every DSTR-th one also by
+      //            one DMA issue for slice kt+STAGES (into S).  Issued back to
+      //            back, a wave's DMA filled the texture unit's command queue
+      //            and stalled its MFMAs behind it.
+      // (With more reads than MFMAs, each MFMA is followed by up to
+      // ceil(reads / MFMAs) of them.)  The MFMAs never wait on an LDS read; the
       // barrier is the only point where the matrix pipe can drain.  With two
       // stages a slice's DMA has one slice of time to land; every further
       // stage adds one (the 4-wave 128 x 128 tiles, one workgroup per CU,
