@@ -539,6 +539,11 @@ struct DmaTile {
       constexpr int PCR = (RD_A + RD_B + SLOTS - 1) / SLOTS;
       static_assert(LOADS_PER_SLICE <= SLOTS, "one DMA issue per MFMA at most");
       constexpr int DSTR = SLOTS / LOADS_PER_SLICE;
+      // With two waves per SIMD, a wave in phase C (which carries the
+      // slice's DMA) issues ahead of a partner that has already moved on to
+      // phase A of the next slice (wave priority, s_setprio), so the DMA goes
+      // out sooner and the pair reaches the next barrier closer together.
+      constexpr bool PRIO = NW >= 8;
       u32x4 fa0[MI], fb0[NJ], fa1[MI], fb1[NJ];
 #pragma unroll
       for (int s = 0; s < STAGES; ++s) issue(s);
@@ -549,6 +554,7 @@ struct DmaTile {
         const char *st = lds + (kt % STAGES) * STAGE_BYTES;
         const char *nx = lds + ((kt + 1) % STAGES) * STAGE_BYTES;
         if constexpr (ASM_READS) wait_lgkm0_fenced();  // fa0 / fb0 (prologue or last phase C)
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int t = 0; t < SLOTS; ++t) {  // phase A
           mfma(t, fa0, fb0);
@@ -560,6 +566,7 @@ struct DmaTile {
         wait_vmcnt<LOADS_PER_SLICE * (STAGES - 2)>();  // slice kt+1 landed
         wait_lgkm0_fenced();  // this wave's reads of S are done (phase C's fragments included)
         lds_barrier();
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int t = 0; t < SLOTS; ++t) {  // phase C
           mfma(t, fa1, fb1);
@@ -570,6 +577,7 @@ struct DmaTile {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
     } else if constexpr (STAGES >= 3 && KSTEPS == 1) {
       // Ring schedule for one-k-step slices.  During slice kt each wave runs
       // its MFMAs on slice kt's fragments (in registers), interleaved with
