@@ -4,6 +4,8 @@
 // and the worklog's Kernel 1 apply alpha/beta per output element; here the
 // update is fused into the tile's register epilogue.)
 #pragma once
+#include <type_traits>
+
 #include "gemm_params.hpp"
 #include "gfx950_prims.hpp"
 
@@ -39,42 +41,58 @@ struct GemmEpilogue {
   static_assert(!RQ || MI % 4 == 0, "row quads need whole quads");
   static_assert(!CQ || NJ % 4 == 0, "column quads need whole quads");
 
-  // C[m][n .. n+3] = alpha * x + beta * C, masked at the column tail.
-  static __device__ __forceinline__ void store4(const GemmParams &p, TO *crow, int n, const float (&x)[4],
-                                                bool use_beta) {
+  // Four C values as stored: 16 bytes of fp32, 8 bytes of a 16-bit type.
+  using Raw4 = typename std::conditional<sizeof(TO) == 4, f32x4, u32x2>::type;
+
+  // Whether C[m][n .. n+3] is one vector access.
+  static __device__ __forceinline__ bool vec4(const GemmParams &p, int n) { return p.c_vec && n + 3 < p.N; }
+  static __device__ __forceinline__ Raw4 load4(const TO *crow, int n) {
+    return *reinterpret_cast<const Raw4 *>(crow + n);
+  }
+
+  // C[m][n .. n+3] = alpha * x + beta * c for a vector access (vec4), with c
+  // the four values load4 read before (used only with use_beta).
+  static __device__ __forceinline__ void store4v(const GemmParams &p, TO *crow, int n, const float (&x)[4],
+                                                 bool use_beta, const Raw4 &c) {
     const float alpha = p.alpha, beta = p.beta;
     float v[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = alpha * x[e];
-    if (p.c_vec && n + 3 < p.N) {
-      if constexpr (sizeof(TO) == 4) {
-        f32x4 *cp = reinterpret_cast<f32x4 *>(crow + n);
-        if (use_beta) {
-          const f32x4 c = *cp;
+    if constexpr (sizeof(TO) == 4) {
+      if (use_beta) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = fmaf(beta, c[e], v[e]);
-        }
-        *cp = f32x4{v[0], v[1], v[2], v[3]};
-      } else {
-        u32x2 *cp = reinterpret_cast<u32x2 *>(crow + n);
-        if (use_beta) {
-          const u32x2 c = *cp;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint16_t bits = (uint16_t)(c[e >> 1] >> (16 * (e & 1)));
-            v[e] = fmaf(beta, to_f32(__builtin_bit_cast(TO, bits)), v[e]);
-          }
-        }
-        u32x2 o;
-#pragma unroll
-        for (int d = 0; d < 2; ++d) {
-          const uint32_t lo = __builtin_bit_cast(uint16_t, from_f32<TO>(v[2 * d]));
-          const uint32_t hi = __builtin_bit_cast(uint16_t, from_f32<TO>(v[2 * d + 1]));
-          o[d] = lo | (hi << 16);
-        }
-        *cp = o;
+        for (int e = 0; e < 4; ++e) v[e] = fmaf(beta, c[e], v[e]);
       }
+      *reinterpret_cast<f32x4 *>(crow + n) = f32x4{v[0], v[1], v[2], v[3]};
     } else {
+      if (use_beta) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint16_t bits = (uint16_t)(c[e >> 1] >> (16 * (e & 1)));
+          v[e] = fmaf(beta, to_f32(__builtin_bit_cast(TO, bits)), v[e]);
+        }
+      }
+      u32x2 o;
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const uint32_t lo = __builtin_bit_cast(uint16_t, from_f32<TO>(v[2 * d]));
+        const uint32_t hi = __builtin_bit_cast(uint16_t, from_f32<TO>(v[2 * d + 1]));
+        o[d] = lo | (hi << 16);
+      }
+      *reinterpret_cast<u32x2 *>(crow + n) = o;
+    }
+  }
+
+  // C[m][n .. n+3] = alpha * x + beta * C, masked at the column tail.
+  static __device__ __forceinline__ void store4(const GemmParams &p, TO *crow, int n, const float (&x)[4],
+                                                bool use_beta) {
+    if (vec4(p, n)) {
+      store4v(p, crow, n, x, use_beta, use_beta ? load4(crow, n) : Raw4{});
+    } else {
+      const float alpha = p.alpha, beta = p.beta;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = alpha * x[e];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if (n + e < p.N) {
@@ -139,31 +157,39 @@ struct GemmEpilogue {
 
   // C[m][n .. n+7] = alpha * x + beta * C for 16-bit C: one 16-byte access
   // where the row allows it (c_vec >= 2), else two four-column stores.
+  static __device__ __forceinline__ bool vec8(const GemmParams &p, int n) { return p.c_vec >= 2 && n + 7 < p.N; }
+  static __device__ __forceinline__ u32x4 load8(const TO *crow, int n) {
+    return *reinterpret_cast<const u32x4 *>(crow + n);
+  }
+  // The 16-byte access of store8 with c read before by load8.
+  static __device__ __forceinline__ void store8v(const GemmParams &p, TO *crow, int n, const float (&x)[8],
+                                                 bool use_beta, const u32x4 &c) {
+    static_assert(sizeof(TO) == 2, "16-bit output");
+    const float alpha = p.alpha, beta = p.beta;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = alpha * x[e];
+    if (use_beta) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint16_t bits = (uint16_t)(c[e >> 1] >> (16 * (e & 1)));
+        v[e] = fmaf(beta, to_f32(__builtin_bit_cast(TO, bits)), v[e]);
+      }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t lo = __builtin_bit_cast(uint16_t, from_f32<TO>(v[2 * d]));
+      const uint32_t hi = __builtin_bit_cast(uint16_t, from_f32<TO>(v[2 * d + 1]));
+      o[d] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x4 *>(crow + n) = o;
+  }
   static __device__ __forceinline__ void store8(const GemmParams &p, TO *crow, int n, const float (&x)[8],
                                                 bool use_beta) {
     static_assert(sizeof(TO) == 2, "16-bit output");
-    if (p.c_vec >= 2 && n + 7 < p.N) {
-      const float alpha = p.alpha, beta = p.beta;
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = alpha * x[e];
-      u32x4 *cp = reinterpret_cast<u32x4 *>(crow + n);
-      if (use_beta) {
-        const u32x4 c = *cp;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint16_t bits = (uint16_t)(c[e >> 1] >> (16 * (e & 1)));
-          v[e] = fmaf(beta, to_f32(__builtin_bit_cast(TO, bits)), v[e]);
-        }
-      }
-      u32x4 o;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t lo = __builtin_bit_cast(uint16_t, from_f32<TO>(v[2 * d]));
-        const uint32_t hi = __builtin_bit_cast(uint16_t, from_f32<TO>(v[2 * d + 1]));
-        o[d] = lo | (hi << 16);
-      }
-      *cp = o;
+    if (vec8(p, n)) {
+      store8v(p, crow, n, x, use_beta, use_beta ? load8(crow, n) : u32x4{});
     } else {
       const float x0[4] = {x[0], x[1], x[2], x[3]}, x1[4] = {x[4], x[5], x[6], x[7]};
       store4(p, crow, n, x0, use_beta);
@@ -199,7 +225,17 @@ struct GemmEpilogue {
       const int m = RQ ? mw + 64 * (i >> 2) + 4 * r + (i & 3) : mw + i * 16 + r;
       if (m >= p.M) continue;
       TO *crow = C + (int64_t)m * p.ldc;
+      // With beta != 0 every vector access of the row is loaded before the
+      // first store: issued one by one after each store, the loads waited
+      // out a memory round trip each (the bf16 NN 4096 x 11008 x 4096 tile's
+      // fp32 C read took ~20 us a round that way).
       if constexpr (PAIRS) {
+        u32x4 cin[NJ / 2] = {};
+        if (use_beta) {
+#pragma unroll
+          for (int jj = 0; jj < NJ / 2; ++jj)
+            if (vec8(p, nw + jj * 32 + g * 8)) cin[jj] = load8(crow, nw + jj * 32 + g * 8);
+        }
 #pragma unroll
         for (int jj = 0; jj < NJ / 2; ++jj) {
           const int n = nw + jj * 32 + g * 8;  // after transpose_pair
@@ -216,18 +252,34 @@ struct GemmEpilogue {
               x[4 + e] = x1[e];
             }
           }
-          store8(p, crow, n, x, use_beta);
+          if (vec8(p, n)) store8v(p, crow, n, x, use_beta, cin[jj]);
+          else store8(p, crow, n, x, use_beta);
         }
       } else if constexpr (!CQ) {
+        Raw4 cin[NJ] = {};
+        if (use_beta) {
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            if (vec4(p, nw + j * 16 + g * 4)) cin[j] = load4(crow, nw + j * 16 + g * 4);
+        }
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
           const int n = nw + j * 16 + g * 4;
           if (n >= p.N) continue;
           float x[4] = {blk[j][0], blk[j][1], blk[j][2], blk[j][3]};
           if (scaled) unscale(p, m, n, x);
-          store4(p, crow, n, x, use_beta);
+          if (vec4(p, n)) store4v(p, crow, n, x, use_beta, cin[j]);
+          else store4(p, crow, n, x, use_beta);
         }
       } else {
+        Raw4 cin[NJ] = {};
+        if (use_beta) {
+#pragma unroll
+          for (int q = 0; q < NJ / 4; ++q)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (vec4(p, nw + 64 * q + 16 * v + 4 * g)) cin[4 * q + v] = load4(crow, nw + 64 * q + 16 * v + 4 * g);
+        }
 #pragma unroll
         for (int q = 0; q < NJ / 4; ++q)
 #pragma unroll
@@ -236,7 +288,8 @@ struct GemmEpilogue {
             if (n >= p.N) continue;
             float x[4] = {blk[4 * q][v], blk[4 * q + 1][v], blk[4 * q + 2][v], blk[4 * q + 3][v]};
             if (scaled) unscale(p, m, n, x);
-            store4(p, crow, n, x, use_beta);
+            if (vec4(p, n)) store4v(p, crow, n, x, use_beta, cin[4 * q + v]);
+            else store4(p, crow, n, x, use_beta);
           }
       }
     }
