@@ -97,6 +97,28 @@ def test_every_config_every_layout_integer_bit_exact(in_dtype):
                     assert_bit_exact(got, ref, c_dtype, what)
 
 
+@pytest.mark.parametrize("in_dtype", ["f32", "f16", "bf16"])
+def test_every_config_beta_ragged_row_of_vector_and_tail_c(in_dtype):
+    """beta != 0 with N % 4 != 0 inside a row pitch that allows vector C
+    accesses (ldc = 272): in every tile's last column block a row mixes
+    vector accesses (their C values loaded ahead of the row's stores) with
+    element-wise tail accesses.  Integer data, bit-exact; the padding columns
+    of C must stay untouched."""
+    import dense_gemm_12_amd as mg
+    M, N, K, ldc = 296, 270, 200, 272
+    for c_dtype in C_TYPES[in_dtype]:
+        A, B, C = make(M, N, K, False, True, in_dtype, c_dtype, "int2", 23)
+        ref = oracle_full(A, B, C, alpha=1.5, beta=0.5, ta=False, tb=True, in_dtype=in_dtype, c_dtype=c_dtype)
+        for cfg in range(mg.num_configs(in_dtype)):
+            name = mg.config_name(in_dtype, cfg)
+            what = f"{name} TN c={c_dtype} {M}x{N}x{K} ldc={ldc}"
+            log("case " + what)
+            ws = SK_WS_BYTES if name.endswith("_sk") else None
+            got = run_gpu(A, B, C, alpha=1.5, beta=0.5, ta=False, tb=True, c_dtype=c_dtype, config=cfg,
+                          ldc=ldc, workspace_bytes=ws)
+            assert_bit_exact(got, ref, c_dtype, what)
+
+
 @pytest.mark.parametrize("in_dtype", ["f16", "bf16"])
 def test_every_16bit_config_long_k_integer_bit_exact(in_dtype):
     """Forced 16-bit configurations with K from one slice to many trips
