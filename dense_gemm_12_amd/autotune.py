@@ -184,6 +184,23 @@ def tune(names, out, trials=3, min_ms=20.0, log=print, cold=True):
             if not results:
                 continue
             results.sort()
+            tie_note = ""
+            if flush is not None and len(results) > 1:
+                # Near-ties of the cold time (within 1 %) go to the faster
+                # back-to-back (warm) call: at this margin cold timings differ
+                # by run-to-run noise, while warm ones can still tell the
+                # kernels apart.
+                near = [r for r in results[:3] if r[0] <= results[0][0] * 1.01]
+                if len(near) > 1:
+                    warm = [(time_config(mg, torch, Ad, Bd, Cd, w, mg.config_id(w["in_dtype"], c), trials, min_ms,
+                                         workspace=ws, splits=sp), (ms, c, sp)) for ms, c, sp in near]
+                    best_warm, best_r = min(warm)
+                    if best_r != results[0]:
+                        log(f"{name + tag}: cold times within 1 %; {best_r[1]} is fastest warm "
+                            f"({best_warm * 1e3:.1f} us)")
+                        results.remove(best_r)
+                        results.insert(0, best_r)
+                        tie_note = f" (near-tie: {best_r[1]} fastest warm, {best_warm * 1e3:.1f}us)"
             picks.append((name, tag, results))
             best_ms, best, best_sp = results[0]
             if best_sp:
@@ -193,7 +210,7 @@ def tune(names, out, trials=3, min_ms=20.0, log=print, cold=True):
                     best_sp = 0
             rule_tag = tag + (f" s={best_sp}" if best_sp else "")
             lines.append(f"# {name}{tag}: " + ", ".join(
-                f"{c}{'/s=%d' % sp if sp else ''}={ms * 1e3:.1f}us" for ms, c, sp in results[:3]))
+                f"{c}{'/s=%d' % sp if sp else ''}={ms * 1e3:.1f}us" for ms, c, sp in results[:3]) + tie_note)
             lines.append(f"{w['in_dtype']} {w['c_dtype']} {'T' if w['ta'] else 'N'} {'T' if w['tb'] else 'N'} "
                          f"{w['M']} {w['N']} {w['K']} {best}{rule_tag}")
         del Ad, Bd, Cd

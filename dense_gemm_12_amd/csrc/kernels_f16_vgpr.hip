@@ -29,8 +29,9 @@ const KernelEntry *entries_f16_vgpr(int *n) {
       make_ws_entry<_Float16, _Float16, 128, 256, 32, 6, 2, 2>("ws_f16_128x256x32_s6_w2x2"),
       make_ws_entry<_Float16, _Float16, 256, 128, 32, 4, 2, 2>("ws_f16_256x128x32_s4_w2x2"),
       make_dma_entry<_Float16, _Float16, 256, 256, 64, 2, 2, 4, false, true>("dma_f16_256x256x64_s2_w2x4_sk"),
-      // few-row problems (split over K): A stored M x K only
+      // few-row problems (split over K): A stored M x K only; four waves, or eight (two per SIMD)
       make_dma_entry<_Float16, _Float16, 64, 128, 64, 3, 2, 2>("dma_f16_64x128x64_s3_w2x2"),
+      make_dma_entry<_Float16, _Float16, 64, 128, 64, 4, 2, 4>("dma_f16_64x128x64_s4_w2x4"),
   };
   *n = (int)(sizeof(table) / sizeof(table[0]));
   return table;
