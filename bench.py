@@ -488,14 +488,14 @@ def main():
         # the kernel it is reported with.
         import threading
         for i, (name, w, Ad, Bd, Cd, ws) in enumerate(calls):
-            box = {"samples": []}
+            holder = {"samples": []}
             t_start = time.perf_counter()
 
             def sampler():
                 while time.perf_counter() - t_start < 3.0:
                     c = read_clocks()
                     if c and time.perf_counter() - t_start >= 1.5:
-                        box["samples"].append(c)
+                        holder["samples"].append(c)
                     elif not c:
                         time.sleep(0.2)
 
@@ -507,13 +507,13 @@ def main():
                     launch(w, Ad, Bd, Cd, ws)
                 torch.cuda.synchronize()
             th.join()
-            sclk = [mhz for c in box["samples"] for k, v in c.items()
+            sclk = [mhz for c in holder["samples"] for k, v in c.items()
                     if k.lower().startswith("sclk clock speed") and (mhz := _mhz(v)) is not None]
-            pw = [c["socket_power_w"] for c in box["samples"] if c.get("socket_power_w") is not None]
+            pw = [c["socket_power_w"] for c in holder["samples"] if c.get("socket_power_w") is not None]
             part_clocks[i] = {"sclk_mhz_samples": sclk,
                               "sclk_mhz_median": statistics.median(sclk) if sclk else None,
                               "socket_power_w_median": statistics.median(pw) if pw else None,
-                              "readings": box["samples"][-1] if box["samples"] else None}
+                              "readings": holder["samples"][-1] if holder["samples"] else None}
         clocks = {calls[i][0]: part_clocks[i] for i in range(len(calls))}
 
     split16 = None
